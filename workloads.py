@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for single-token decode attention.
+
+This module is the only code shared by the oracle side and the GPU side. It
+draws inputs and nothing else: it holds none of the attention arithmetic.
+
+Values are drawn with numpy's PCG64 generator as float32 standard normals,
+multiplied by a standard deviation, and rounded to bfloat16 with IEEE
+round-to-nearest-even. Arrays are drawn in the order q, K, V, then the
+selection. Every array is returned as raw bfloat16 bit patterns (uint16) so
+that both sides see exactly the same bits.
+
+Workloads (shapes follow the problem statement of the fuel-dispatch page
+"DecodeFlashSpec", fields q, k, v, softmax_scale, k_len; the sparse layout
+follows the metrale page "AttnV41", decode_fixed_topk and decode_prep):
+
+* ``tiny``     dense, B=1 Hq=8 Hkv=8 D=64, capacity 512, k_len 300, scale 1/8
+* ``gqa``      dense, B=8 Hq=32 Hkv=8 D=128, capacity 8192, k_len 4096;
+               rows at and beyond k_len hold NaN
+* ``long``     dense, B=4 Hq=64 Hkv=8 D=128, capacity = k_len = 131072
+* ``batch``    dense, B=128 Hq=32 Hkv=8 D=128, capacity 2048, k_len 1537,
+               values with standard deviation 0.5
+* ``sparse``   B=4 Hq=64, one shared KV head of 65536 rows, D=128, topk 2048:
+               128 window slots, then distinct random indices, then -1 pads
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (IEEE round-to-nearest-even); NaN stays NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws rounded to bfloat16 bits."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return f32_to_bf16_bits(x)
+
+
+@dataclass
+class DenseCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    capacity: int
+    k_len: int
+    scale: float            # the float32 value handed to the kernel
+    std: float = 1.0
+    poison: bool = False    # fill rows >= k_len with NaN
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def kv_bytes(self) -> int:
+        """Live K+V bytes: the rows [0, k_len) of every (b, kv-head)."""
+        return 2 * self.B * self.Hkv * self.k_len * self.D * 2
+
+    def algorithmic_bytes(self) -> int:
+        """Live K+V rows plus q plus out, all bfloat16."""
+        return self.kv_bytes() + 2 * (self.B * self.Hq * self.D * 2)
+
+
+@dataclass
+class SparseCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    rows: int               # KV rows per (kv_batch, kv-head); also k_len
+    topk: int
+    window: int
+    counts: tuple           # random (index) entries per token, before padding
+    kv_batch: int = 1       # 1: rows shared by all tokens; B: one set per token
+    scale: float = 0.0
+    std: float = 1.0
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def valid_counts(self):
+        return [self.window + c for c in self.counts]
+
+    def algorithmic_bytes(self) -> int:
+        """Gathered K+V rows (valid entries only) plus selection, q and out."""
+        rows = sum(self.valid_counts())
+        return (rows * self.Hkv * self.D * 2 * 2 + self.B * self.topk * 4
+                + 2 * (self.B * self.Hq * self.D * 2))
+
+
+def _f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+DENSE_CASES = {
+    "tiny": DenseCase("tiny", 1, 8, 8, 64, 512, 300, _f32(1.0 / 8.0), seed=1),
+    "gqa": DenseCase("gqa", 8, 32, 8, 128, 8192, 4096, _f32(1.0 / math.sqrt(128)),
+                     poison=True, seed=2),
+    "long": DenseCase("long", 4, 64, 8, 128, 131072, 131072, _f32(1.0 / math.sqrt(128)), seed=3),
+    "batch": DenseCase("batch", 128, 32, 8, 128, 2048, 1537, _f32(1.0 / math.sqrt(128)),
+                       std=0.5, seed=4),
+}
+
+SPARSE_CASES = {
+    "sparse": SparseCase("sparse", 4, 64, 1, 128, 65536, 2048, 128, (1920, 1920, 1920, 1920),
+                         scale=_f32(1.0 / math.sqrt(128)), seed=5),
+    "sparse_mixed": SparseCase("sparse_mixed", 4, 64, 1, 128, 65536, 2048, 128,
+                               (1920, 1337, 960, 0), scale=_f32(1.0 / math.sqrt(128)), seed=5),
+}
+
+
+def dense_inputs(case: DenseCase, seed: int | None = None):
+    """q [B,Hq,1,D], k and v [B,Hkv,capacity,D] as bfloat16 bits."""
+    rng = np.random.Generator(np.random.PCG64(case.seed if seed is None else seed))
+    q = normal_bf16(rng, (case.B, case.Hq, 1, case.D), case.std)
+    k = normal_bf16(rng, (case.B, case.Hkv, case.capacity, case.D), case.std)
+    v = normal_bf16(rng, (case.B, case.Hkv, case.capacity, case.D), case.std)
+    if case.poison and case.k_len < case.capacity:
+        k[:, :, case.k_len:, :] = BF16_NAN
+        v[:, :, case.k_len:, :] = BF16_NAN
+    return q, k, v
+
+
+def selection(rng: np.random.Generator, B: int, rows: int, topk: int, window: int,
+              counts) -> np.ndarray:
+    """Padded selection [B, topk] int32.
+
+    Per token: the window slots (the last ``window`` rows, ascending), then
+    ``counts[b]`` distinct random indices from the rows before the window, in
+    random order, then -1 up to ``topk``.
+    """
+    sel = np.full((B, topk), -1, dtype=np.int32)
+    win = np.arange(rows - window, rows, dtype=np.int32)
+    for b in range(B):
+        n = int(counts[b])
+        if window + n > topk:
+            raise ValueError("selection wider than topk")
+        idx = rng.choice(rows - window, size=n, replace=False).astype(np.int32)
+        sel[b, :window] = win
+        sel[b, window:window + n] = idx
+    return sel
+
+
+def sparse_inputs(case: SparseCase, seed: int | None = None):
+    """q [B,Hq,1,D]; k, v [kv_batch,Hkv,rows,D]; sel [B,topk] int32."""
+    rng = np.random.Generator(np.random.PCG64(case.seed if seed is None else seed))
+    q = normal_bf16(rng, (case.B, case.Hq, 1, case.D), case.std)
+    k = normal_bf16(rng, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
+    v = normal_bf16(rng, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
+    sel = selection(rng, case.B, case.rows, case.topk, case.window, case.counts)
+    return q, k, v, sel
+
+
+def repad(sel: np.ndarray, topk: int) -> np.ndarray:
+    """The same valid prefix re-padded with -1 to a new width ``topk``."""
+    B, old = sel.shape
+    out = np.full((B, topk), -1, dtype=np.int32)
+    keep = min(old, topk)
+    out[:, :keep] = sel[:, :keep]
+    if keep < old and (sel[:, keep:] >= 0).any():
+        raise ValueError("re-padding would drop valid entries")
+    return out
