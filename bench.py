@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark: single-token decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+One step is one complete call of the library for the whole batch (the split-K
+partial kernel plus, when the plan splits the keys, the log-sum-exp combine),
+with every input already resident in HBM. Prints ONE JSON line:
+
+  value        algorithmic bytes per step / wall time per step, in GB/s, where the
+               algorithmic bytes are the live K and V rows plus q and out (for the
+               sparse workloads: the gathered rows, the selection, q and out)
+  roofline     the partial kernel (the one that streams K and V): algorithmic bytes
+               per launch / its mean duration from HIP events recorded on its own
+               stream around each launch in the timed region, against 8 TB/s
+  cpu_baseline the fp64 oracle timed on this host's cores over a bounded sample of
+               the same workload
+
+Workloads are the seeded synthetic inputs of ``workloads.py``; the default is the
+long-context dense GQA workload (B=4, Hq=64, Hkv=8, D=128, k_len = capacity =
+131072), whose K and V (2 GiB) are far larger than the 256 MB Infinity Cache.
+Smaller workloads are rotated over several copies of K and V so that each step
+reads from HBM rather than from that cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention KV-read GB/s (fraction of HBM peak) and µs/step"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_partial.json")
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for fn in ("kernels.hip", "device_common.h", "launch.h"):
+        with open(os.path.join(ROOT, "decode_attention_05_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(workload: str):
+    """HBM bytes per partial-kernel launch from committed rocprofv3 counter runs,
+    or None when they are missing or were taken on a different kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def build_inputs(args, torch, W, H):
+    if args.workload in W.DENSE_CASES:
+        case = W.DENSE_CASES[args.workload]
+        log(f"generating {args.workload} inputs (seed {case.seed})")
+        q, k, v = W.dense_inputs(case)
+        host = dict(q=q, k=k, v=v, sel=None)
+        kv_bytes_alloc = 2 * k.nbytes
+        desc = (f"{case.name}: dense decode, B={case.B} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
+                f"capacity={case.capacity} k_len={case.k_len}")
+        cfg = dict(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
+                   capacity=case.capacity, k_len=case.k_len)
+        return case, host, kv_bytes_alloc, desc, cfg, case.algorithmic_bytes()
+    case = W.SPARSE_CASES[args.workload]
+    log(f"generating {args.workload} inputs (seed {case.seed})")
+    q, k, v, sel = W.sparse_inputs(case)
+    host = dict(q=q, k=k, v=v, sel=sel)
+    desc = (f"{case.name}: index-selected sparse decode, B={case.B} Hq={case.Hq} Hkv={case.Hkv} "
+            f"D={case.D} rows={case.rows} topk={case.topk} valid={case.valid_counts()}")
+    cfg = dict(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
+               rows=case.rows, topk=case.topk)
+    return case, host, 2 * k.nbytes, desc, cfg, case.algorithmic_bytes()
+
+
+def cpu_baseline(args, case, host, algo_bytes, W):
+    """Time the fp64 oracle (as it stands) on this host over a bounded sample."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    rows_total = case.B * case.Hq
+    # About one second of all-core work per probe; grow the sample to ~10 s of wall.
+    n = min(rows_total, max(1, threads))
+    t_probe = 0.0
+    while True:
+        rows = np.arange(n, dtype=np.int64) % rows_total
+        t0 = time.perf_counter()
+        if host["sel"] is None:
+            oracle.dense(host["q"], host["k"], host["v"], case.scale, case.k_len, rows=rows,
+                         threads=threads)
+        else:
+            oracle.sparse(host["q"], host["k"], host["v"], host["sel"], case.scale, case.rows,
+                          rows=rows, threads=threads)
+        t_probe = time.perf_counter() - t0
+        if t_probe >= args.cpu_seconds or n >= rows_total * 4:
+            break
+        grow = max(2.0, min(8.0, args.cpu_seconds / max(t_probe, 1e-3)))
+        n = int(n * grow)
+    per_step = t_probe * rows_total / n
+    return {
+        "value": round(algo_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} query rows (b, h) of the {rows_total} in one step"
+                   f"{' (rows repeated)' if n > rows_total else ''}, {t_probe:.2f} s wall on "
+                   f"{threads} threads, scaled to a full step ({per_step * 1e3:.1f} ms/step)"),
+        "s_per_step": round(per_step, 6),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--force-splits", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported. Decode attention here shards with no exchange across (batch, kv head) "
+              "units, so the whole-job figure for N GPUs is N times the one-GPU figure at a "
+              "weak-scaled batch; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_05_amd as da
+    import workloads as W
+    from tests import helpers as H
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    da.library()
+
+    case, host, kv_alloc, desc, cfg, algo_bytes = build_inputs(args, torch, W, H)
+    sparse = host["sel"] is not None
+    sets = 1 if kv_alloc >= 2 * MALL_BYTES else max(4, math.ceil(2 * MALL_BYTES / kv_alloc))
+    log(f"copying to device ({sets} K/V set{'s' if sets > 1 else ''})")
+    dq = H.to_dev(host["q"])
+    dks = [H.to_dev(host["k"])]
+    dvs = [H.to_dev(host["v"])]
+    for _ in range(sets - 1):
+        dks.append(dks[0].clone())
+        dvs.append(dvs[0].clone())
+    dsel = H.to_dev_i32(host["sel"]) if sparse else None
+    B, Hq, D = case.B, case.Hq, case.D
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
+    if sparse:
+        plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.rows, topk_max=case.topk,
+                                   kv_batch=case.kv_batch)
+        splits = -(-case.topk // plan.chunk)
+    else:
+        plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.capacity, case.k_len,
+                                   force_splits=args.force_splits)
+        splits = plan.num_splits_max
+    ws = da.workspace_for(plan)
+
+    def step(i):
+        kk, vv = dks[i % sets], dvs[i % sets]
+        if sparse:
+            da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows, ws)
+        else:
+            da.decode_attn_dense(plan, dq, kk, vv, out, case.scale, case.k_len, ws)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in ev_b + ev_a:      # create the underlying hipEvent_t before handing it over
+        e.record(stream)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        da.decode_attn_set_timing_events(ev_b[i].cuda_event, ev_a[i].cuda_event)
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    da.decode_attn_set_timing_events(None, None)
+
+    kern_ms = np.array([ev_b[i].elapsed_time(ev_a[i]) for i in range(args.steps)])
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_mean_s = float(kern_ms.mean()) * 1e-3
+    achieved = algo_bytes / kern_mean_s / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step, partial kernel mean {kern_mean_s * 1e6:.1f} us "
+        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f})")
+
+    traffic = traffic_from_counters(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(workload=desc, splits=splits, kv_sets=sets,
+                       algorithmic_bytes_per_step=algo_bytes, **cfg),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "partial (split-K stream of K and V)",
+            "kernel_us_mean": round(kern_mean_s * 1e6, 3),
+            "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+            "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
+            "bytes_per_launch": algo_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(args, case, host, algo_bytes, W)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

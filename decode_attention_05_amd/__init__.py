@@ -1,0 +1,215 @@
+"""Single-token decode attention on MI355X: a thin Python binding of the C ABI.
+
+Every compute step runs in the HIP kernels of ``libdecode_attn.so``; this module
+only marshals arguments (tensor pointers, sizes, the current HIP stream) into
+the C functions declared in ``include/decode_attn.h`` and checks that the
+tensors it is handed match the plan, so that no kernel is ever given a buffer
+smaller than the plan implies. PyTorch provides device memory and streams.
+
+Names mirror the C ABI: ``decode_attn_plan``, ``decode_attn_dense``,
+``decode_attn_sparse``, ``decode_attn_status_str``, ``decode_attn_last_error``.
+If the shared library has not been built, loading it raises: there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "DecodeAttnError", "Problem", "Plan", "library", "library_path",
+    "decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
+    "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
+    "workspace_for",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdecode_attn.so")
+
+DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
+
+EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
+                    "decode_attn_set_timing_events", "decode_attn_status_str",
+                    "decode_attn_last_error")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``decode_attn_problem``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("seq_q", ctypes.c_int32), ("capacity", ctypes.c_int64),
+        ("max_k_len", ctypes.c_int64), ("topk_max", ctypes.c_int32),
+        ("kv_batch", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("has_alibi", ctypes.c_int32), ("window_left", ctypes.c_int64),
+        ("window_right", ctypes.c_int64), ("has_softcap", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+        ("force_chunk", ctypes.c_int32),
+    ]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of ``decode_attn_plan_t`` (plain data)."""
+    _fields_ = [
+        ("prob", Problem), ("group", ctypes.c_int32), ("num_splits_max", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("num_cus", ctypes.c_int32), ("kind", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+    @property
+    def sparse(self) -> bool:
+        return self.kind == 1
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {message}")
+
+
+_lib = None
+
+
+def library():
+    """Load ``libdecode_attn.so`` (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with `python -m decode_attention_05_amd.build`"
+                " (there is no fallback implementation)")
+        lib = ctypes.CDLL(library_path)
+        P = ctypes.c_void_p
+        lib.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Plan)]
+        lib.decode_attn_plan.restype = ctypes.c_int
+        lib.decode_attn_dense.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
+                                          ctypes.c_int64, P, ctypes.c_size_t, P]
+        lib.decode_attn_dense.restype = ctypes.c_int
+        lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
+                                           ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
+        lib.decode_attn_sparse.restype = ctypes.c_int
+        lib.decode_attn_set_timing_events.argtypes = [P, P]
+        lib.decode_attn_set_timing_events.restype = ctypes.c_int
+        lib.decode_attn_status_str.argtypes = [ctypes.c_int]
+        lib.decode_attn_status_str.restype = ctypes.c_char_p
+        lib.decode_attn_last_error.argtypes = []
+        lib.decode_attn_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return library().decode_attn_status_str(s).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return f"status {s}"
+
+
+def decode_attn_set_timing_events(ev_before, ev_after):
+    """Record raw hipEvent_t handles around every later partial-kernel launch on this thread."""
+    _check(library().decode_attn_set_timing_events(ev_before, ev_after))
+
+
+def decode_attn_status_str(s: int) -> str:
+    return library().decode_attn_status_str(s).decode()
+
+
+def decode_attn_last_error() -> str:
+    return library().decode_attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != DA_OK:
+        raise DecodeAttnError(status, decode_attn_last_error())
+
+
+def decode_attn_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     capacity: int, max_k_len: int | None = None, *, topk_max: int = 0,
+                     kv_batch: int = 0, seq_q: int = 1, causal: bool = False,
+                     has_alibi: bool = False, window_left: int = -1, window_right: int = -1,
+                     has_softcap: bool = False, num_cus: int = 0, force_splits: int = 0,
+                     force_chunk: int = 0) -> Plan:
+    """Validate a problem and return its plan (see ``decode_attn_plan`` in the header)."""
+    prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, seq_q, capacity,
+                   capacity if max_k_len is None else max_k_len, topk_max, kv_batch,
+                   int(bool(causal)), int(bool(has_alibi)), window_left, window_right,
+                   int(bool(has_softcap)), num_cus, force_splits, force_chunk)
+    plan = Plan()
+    _check(library().decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)))
+    return plan
+
+
+def workspace_for(plan: Plan, device="cuda"):
+    """A device byte buffer of the plan's workspace size (None when it needs none)."""
+    import torch
+    n = int(plan.workspace_bytes)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _tensor_ptr(t, name, shape, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ws_ptr(plan, workspace):
+    if workspace is None:
+        return None, 0
+    import torch
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int,
+                      workspace=None, stream=None):
+    """Enqueue dense decode attention on ``stream`` (default: torch's current stream)."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    bf = torch.bfloat16
+    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_dense(ctypes.byref(plan), *args, float(softmax_scale), int(k_len),
+                                       ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def decode_attn_sparse(plan: Plan, q, k, v, sel, topk: int, out, softmax_scale: float,
+                       k_len: int | None = None, workspace=None, stream=None):
+    """Enqueue index-selected sparse decode attention (sel: int32 [B, topk])."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    bf = torch.bfloat16
+    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf),
+            _tensor_ptr(k, "k", (p.kv_batch, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (p.kv_batch, Hkv, cap, D), bf),
+            _tensor_ptr(sel, "sel", (B, topk), torch.int32))
+    outp = _tensor_ptr(out, "out", (B, Hq, 1, D), bf)
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_sparse(ctypes.byref(plan), *args, int(topk), outp,
+                                        float(softmax_scale), int(cap if k_len is None else k_len),
+                                        ws, wsb, _stream_ptr(stream)))
+    return out

@@ -1,0 +1,365 @@
+// api.cpp -- the C ABI of the decode-attention library: problem validation, the
+// split-K plan, and the two compute entry points. Host code only; the kernels
+// live in kernels.hip.
+//
+// The problem statement follows the fuel-dispatch page "DecodeFlashSpec"
+// (shapes of q, k, v; softmax_scale; k_len as the live prefix; causal accepted
+// and ignored; ALiBi, windows and softcap rejected); the sparse call follows
+// the metrale page "AttnV41" (decode_fixed_topk: a fixed launch width padded
+// with -1). Validation fails closed on host-visible values only, and no call
+// synchronises or copies, as the flashinfer page "packed_fused_kda_decode"
+// describes for caller-owned, graph-stable buffers.
+#include "../../include/decode_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr;  // optional timing of the partial kernel
+thread_local hipEvent_t g_ev_after = nullptr;
+
+decode_attn_status fail(decode_attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+decode_attn_status ok() {
+  g_last_error[0] = '\0';
+  return DA_OK;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("DECODE_ATTN_LOG");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+// Compute units per device, queried once per device id.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cache[kMaxDevices];
+
+decode_attn_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return DA_OK;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || c <= 0)
+    return fail(DA_ERR_HIP, "querying the compute-unit count failed: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_cu_cache[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return DA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// --- split-K heuristic -------------------------------------------------------
+//
+// The hot path is bound by HBM bandwidth, so the grid must keep every CU
+// streaming: aim for about kWgsPerCu workgroups per CU, but never give a split
+// fewer than kMinChunk keys (below that the combine and launch overheads are
+// larger than the streaming work of a split).
+constexpr int kWgsPerCu = 4;
+constexpr int kMinChunk = 256;
+constexpr int kKeyAlign = 16;
+constexpr int kMaxSplits = 1 << 16;
+
+int heads_per_wg(int G) {
+  for (int gt : {8, 4, 2, 1})
+    if (G % gt == 0) return gt;
+  return 1;
+}
+
+// Number of splits and keys per split for one dense call of length k_len.
+void dense_split(const decode_attn_plan_t& P, int64_t k_len, int* S_out, int* chunk_out,
+                 int* bound_out) {
+  const auto& p = P.prob;
+  const int gt = heads_per_wg(P.group);
+  const int64_t units = (int64_t)p.batch * p.num_kv_heads * (P.group / gt);
+  int64_t chunk, S, bound;
+  if (p.force_chunk > 0) {
+    chunk = p.force_chunk;
+    S = ceil_div(k_len, chunk);
+    bound = S;
+  } else {
+    int64_t target = p.force_splits > 0 ? p.force_splits
+                                        : ceil_div((int64_t)kWgsPerCu * P.num_cus, units);
+    const int64_t min_chunk = p.force_splits > 0 ? 1 : kMinChunk;
+    int64_t s0 = std::min<int64_t>(target, ceil_div(k_len, min_chunk));
+    s0 = std::max<int64_t>(1, std::min<int64_t>(s0, kMaxSplits));
+    bound = s0;
+    chunk = round_up(ceil_div(k_len, s0), p.force_splits > 0 ? 1 : kKeyAlign);
+    S = ceil_div(k_len, chunk);
+  }
+  *S_out = (int)S;
+  *chunk_out = (int)chunk;
+  if (bound_out) *bound_out = (int)bound;
+}
+
+decode_attn_status validate_problem(const decode_attn_problem& p) {
+  if (p.has_alibi) return fail(DA_ERR_UNSUPPORTED, "alibi: ALiBi slopes are not supported");
+  if (p.window_left != -1)
+    return fail(DA_ERR_UNSUPPORTED, "window_left: sliding windows are not supported");
+  if (p.window_right != -1)
+    return fail(DA_ERR_UNSUPPORTED, "window_right: sliding windows are not supported");
+  if (p.has_softcap) return fail(DA_ERR_UNSUPPORTED, "softcap: logit softcap is not supported");
+  if (p.seq_q != 1)
+    return fail(DA_ERR_UNSUPPORTED, "seq_q: only single-token decode (seq_q == 1) is supported, got %d",
+                p.seq_q);
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(DA_ERR_UNSUPPORTED, "head_dim: only 64 and 128 are supported, got %d", p.head_dim);
+  if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1)
+    return fail(DA_ERR_INVALID_ARG, "batch, num_q_heads and num_kv_heads must be >= 1");
+  if (p.num_q_heads % p.num_kv_heads != 0)
+    return fail(DA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                p.num_q_heads, p.num_kv_heads);
+  if (p.capacity < 1) return fail(DA_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (p.max_k_len < 1 || p.max_k_len > p.capacity)
+    return fail(DA_ERR_INVALID_ARG, "max_k_len must lie in [1, capacity], got %lld",
+                (long long)p.max_k_len);
+  if (p.topk_max < 0) return fail(DA_ERR_INVALID_ARG, "topk_max must be >= 0");
+  if (p.topk_max > 0) {
+    if (p.kv_batch != 1 && p.kv_batch != p.batch)
+      return fail(DA_ERR_INVALID_ARG, "kv_batch must be 1 or batch for a sparse plan, got %d",
+                  p.kv_batch);
+  } else if (p.kv_batch != 0 && p.kv_batch != p.batch) {
+    return fail(DA_ERR_INVALID_ARG, "kv_batch must be 0 or batch for a dense plan, got %d",
+                p.kv_batch);
+  }
+  if (p.num_cus < 0 || p.force_splits < 0 || p.force_chunk < 0)
+    return fail(DA_ERR_INVALID_ARG, "num_cus, force_splits and force_chunk must be >= 0");
+  // Element counts must fit the 64-bit index arithmetic with ample margin.
+  const double elems = (double)p.batch * p.num_kv_heads * (double)p.capacity * p.head_dim;
+  if (elems > 9.0e15) return fail(DA_ERR_INVALID_ARG, "KV buffer too large");
+  if ((int64_t)p.batch * p.num_q_heads > 0x7fffffff)
+    return fail(DA_ERR_INVALID_ARG, "batch * num_q_heads too large");
+  return DA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+da::PartialLaunch base_launch(const decode_attn_plan_t& P, const void* q, const void* k,
+                              const void* v, void* out, float scale, int64_t k_len,
+                              void* workspace, int S) {
+  const auto& p = P.prob;
+  da::PartialLaunch L{};
+  L.q = static_cast<const uint16_t*>(q);
+  L.k = static_cast<const uint16_t*>(k);
+  L.v = static_cast<const uint16_t*>(v);
+  L.out = static_cast<uint16_t*>(out);
+  L.B = p.batch;
+  L.Hq = p.num_q_heads;
+  L.Hkv = p.num_kv_heads;
+  L.G = P.group;
+  L.D = p.head_dim;
+  L.kv_batch = p.kv_batch;
+  L.capacity = p.capacity;
+  L.k_len = k_len;
+  L.S = S;
+  L.heads_per_wg = heads_per_wg(P.group);
+  L.qscale = scale * 1.4426950408889634f;  // log2(e): the kernels use exp2
+  const int64_t rows = (int64_t)p.batch * p.num_q_heads;
+  float* ws = static_cast<float*>(workspace);
+  L.part_o = S > 1 ? ws : nullptr;
+  L.part_m = S > 1 ? ws + rows * S * p.head_dim : nullptr;
+  L.part_l = S > 1 ? ws + rows * S * (p.head_dim + 1) : nullptr;
+  return L;
+}
+
+uint64_t workspace_for(const decode_attn_problem& p, int S) {
+  if (S <= 1) return 0;
+  return (uint64_t)p.batch * p.num_q_heads * (uint64_t)S * (p.head_dim + 2) * sizeof(float);
+}
+
+decode_attn_status check_common(const decode_attn_plan_t* plan, int kind, const void* q,
+                                const void* k, const void* v, void* out, float scale,
+                                void* workspace, size_t workspace_bytes) {
+  if (!plan) return fail(DA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->kind != kind)
+    return fail(DA_ERR_INVALID_ARG, kind ? "plan is a dense plan; use decode_attn_dense"
+                                         : "plan is a sparse plan; use decode_attn_sparse");
+  if (!q || !k || !v || !out) return fail(DA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(DA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(DA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (plan->workspace_bytes > 0) {
+    if (!workspace) return fail(DA_ERR_WORKSPACE, "workspace is NULL but the plan needs %llu bytes",
+                                (unsigned long long)plan->workspace_bytes);
+    if (workspace_bytes < plan->workspace_bytes)
+      return fail(DA_ERR_WORKSPACE, "workspace has %zu bytes, the plan needs %llu", workspace_bytes,
+                  (unsigned long long)plan->workspace_bytes);
+    if (!aligned16(workspace)) return fail(DA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  return DA_OK;
+}
+
+decode_attn_status run(const da::PartialLaunch& L, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_ev_before) {
+    e = hipEventRecord(g_ev_before, st);
+    if (e != hipSuccess) return fail(DA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
+  e = da::launch_partial(L, st);
+  if (e != hipSuccess) return fail(DA_ERR_HIP, "partial kernel launch failed: %s", hipGetErrorString(e));
+  if (g_ev_after) {
+    e = hipEventRecord(g_ev_after, st);
+    if (e != hipSuccess) return fail(DA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
+  if (L.S > 1) {
+    e = da::launch_combine(L, st);
+    if (e != hipSuccess)
+      return fail(DA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_plan_t* out) {
+  if (!p || !out) return fail(DA_ERR_INVALID_ARG, "problem and plan pointers must be non-NULL");
+  decode_attn_status s = validate_problem(*p);
+  if (s != DA_OK) return s;
+  decode_attn_plan_t P;
+  std::memset(&P, 0, sizeof P);
+  P.prob = *p;
+  P.group = p->num_q_heads / p->num_kv_heads;
+  P.kind = p->topk_max > 0 ? 1 : 0;
+  if (P.kind == 0) P.prob.kv_batch = p->batch;
+  int cus = p->num_cus;
+  if (cus == 0) {
+    s = device_cus(&cus);
+    if (s != DA_OK) return s;
+  }
+  P.num_cus = cus;
+  const int gt = heads_per_wg(P.group);
+  const int64_t units = (int64_t)p->batch * p->num_kv_heads * (P.group / gt);
+  if (P.kind == 0) {
+    int S = 0, chunk = 0, bound = 0;
+    dense_split(P, p->max_k_len, &S, &chunk, &bound);
+    P.num_splits_max = bound;
+    P.chunk = chunk;
+  } else {
+    // The chunk depends on the plan only (never on a call's topk), which is what
+    // makes padding to any launch width bit-exact.
+    int64_t chunk;
+    if (p->force_chunk > 0) {
+      chunk = p->force_chunk;
+    } else {
+      const int64_t per_unit = std::max<int64_t>(1, ceil_div((int64_t)kWgsPerCu * cus, units));
+      chunk = std::max<int64_t>(kKeyAlign, round_up(ceil_div(p->topk_max, per_unit), kKeyAlign));
+    }
+    const int64_t S = ceil_div(p->topk_max, chunk);
+    if (S > kMaxSplits) return fail(DA_ERR_INVALID_ARG, "force_chunk gives too many splits");
+    P.chunk = (int)chunk;
+    P.num_splits_max = (int)S;
+  }
+  if (P.num_splits_max > kMaxSplits) return fail(DA_ERR_INVALID_ARG, "too many splits");
+  P.workspace_bytes = workspace_for(P.prob, P.num_splits_max);
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "[decode_attn] plan kind=%s B=%d Hq=%d Hkv=%d D=%d G=%d heads/wg=%d units=%lld "
+                 "cus=%d splits_max=%d chunk=%d workspace=%llu\n",
+                 P.kind ? "sparse" : "dense", p->batch, p->num_q_heads, p->num_kv_heads,
+                 p->head_dim, P.group, gt, (long long)units, cus, P.num_splits_max, P.chunk,
+                 (unsigned long long)P.workspace_bytes);
+  *out = P;
+  return ok();
+}
+
+decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void* q, const void* k,
+                                     const void* v, void* out, float softmax_scale, int64_t k_len,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  decode_attn_status s =
+      check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
+  if (s != DA_OK) return s;
+  if (k_len < 1 || k_len > plan->prob.max_k_len)
+    return fail(DA_ERR_INVALID_ARG, "k_len must lie in [1, max_k_len = %lld], got %lld",
+                (long long)plan->prob.max_k_len, (long long)k_len);
+  int S = 0, chunk = 0;
+  dense_split(*plan, k_len, &S, &chunk, nullptr);
+  if (S > plan->num_splits_max)
+    return fail(DA_ERR_INVALID_ARG, "internal: %d splits exceed the plan's %d", S,
+                plan->num_splits_max);
+  da::PartialLaunch L = base_launch(*plan, q, k, v, out, softmax_scale, k_len, workspace, S);
+  L.chunk = chunk;
+  L.sparse = false;
+  if (log_enabled())
+    std::fprintf(stderr, "[decode_attn] dense k_len=%lld splits=%d chunk=%d\n", (long long)k_len, S,
+                 chunk);
+  return run(L, stream);
+}
+
+decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void* q, const void* k,
+                                      const void* v, const int32_t* sel, int32_t topk, void* out,
+                                      float softmax_scale, int64_t k_len, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  decode_attn_status s =
+      check_common(plan, 1, q, k, v, out, softmax_scale, workspace, workspace_bytes);
+  if (s != DA_OK) return s;
+  if (!sel) return fail(DA_ERR_INVALID_ARG, "sel must be non-NULL");
+  if (((uintptr_t)sel & 3u) != 0) return fail(DA_ERR_INVALID_ARG, "sel must be 4-byte aligned");
+  if (topk < 1 || topk > plan->prob.topk_max)
+    return fail(DA_ERR_INVALID_ARG, "topk must lie in [1, topk_max = %d], got %d",
+                plan->prob.topk_max, topk);
+  if (k_len < 1 || k_len > plan->prob.capacity)
+    return fail(DA_ERR_INVALID_ARG, "k_len must lie in [1, capacity = %lld], got %lld",
+                (long long)plan->prob.capacity, (long long)k_len);
+  const int S = (int)ceil_div(topk, plan->chunk);
+  da::PartialLaunch L = base_launch(*plan, q, k, v, out, softmax_scale, k_len, workspace, S);
+  L.sel = sel;
+  L.topk = topk;
+  L.chunk = plan->chunk;
+  L.sparse = true;
+  if (log_enabled())
+    std::fprintf(stderr, "[decode_attn] sparse topk=%d splits=%d chunk=%d\n", topk, S, plan->chunk);
+  return run(L, stream);
+}
+
+decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after) {
+  if ((ev_before == nullptr) != (ev_after == nullptr))
+    return fail(DA_ERR_INVALID_ARG, "pass both timing events or neither");
+  g_ev_before = static_cast<hipEvent_t>(ev_before);
+  g_ev_after = static_cast<hipEvent_t>(ev_after);
+  return ok();
+}
+
+const char* decode_attn_status_str(decode_attn_status s) {
+  switch (s) {
+    case DA_OK: return "DA_OK";
+    case DA_ERR_INVALID_ARG: return "DA_ERR_INVALID_ARG";
+    case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED";
+    case DA_ERR_WORKSPACE: return "DA_ERR_WORKSPACE";
+    case DA_ERR_HIP: return "DA_ERR_HIP";
+  }
+  return "DA_ERR_UNKNOWN";
+}
+
+const char* decode_attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

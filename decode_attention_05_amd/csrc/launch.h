@@ -1,0 +1,34 @@
+// launch.h -- host-side launch descriptors shared by the API layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+// Everything one split-K pass needs. Pointers are device pointers.
+struct PartialLaunch {
+  const uint16_t* q;   // [B, Hq, 1, D] bf16
+  const uint16_t* k;   // [kv_batch, Hkv, capacity, D] bf16
+  const uint16_t* v;
+  const int32_t* sel;  // sparse only: [B, topk]
+  uint16_t* out;       // [B, Hq, 1, D] bf16: written directly when S == 1
+  float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1)
+  float* part_m;       // [B*Hq, S] running max, base 2 (S > 1)
+  float* part_l;       // [B*Hq, S] softmax denominators (S > 1)
+  int B, Hq, Hkv, G, D;
+  int kv_batch;        // sparse: 1 or B; dense: B
+  int64_t capacity;
+  int64_t k_len;       // dense: attended prefix; sparse: rows usable by sel
+  int topk;            // sparse: launch width
+  int chunk;           // keys (dense) or selection entries (sparse) per split
+  int S;               // number of splits
+  int heads_per_wg;    // query heads of one group handled by one workgroup
+  float qscale;        // softmax_scale * log2(e)
+  bool sparse;
+};
+
+hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream);
+hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream);
+
+}  // namespace da

@@ -1,0 +1,171 @@
+/*
+ * decode_attn.h -- single-token decode attention on MI355X (gfx950), C ABI.
+ *
+ * The operation. For one query token per sequence,
+ *
+ *     out[b, h, 0, :] = sum_j softmax_j( softmax_scale * q[b, h, 0, :] . K[b, hk, j, :] ) V[b, hk, j, :]
+ *
+ * with hk = h / (Hq / Hkv) (grouped-query heads: each KV head serves a
+ * contiguous group of Hq / Hkv query heads). This is the problem stated by the
+ * fuel-dispatch page "DecodeFlashSpec": q is [B, Hq, Sq, D]; k and v are the
+ * capacity KV buffers [B, Hkv, capacity, D]; softmax_scale is an f32 (usually
+ * 1/sqrt(head_dim)); the query attends the live prefix [0, k_len) (field
+ * k_len); causal is accepted and ignored since a single query row sees the
+ * whole prefix (field causal); ALiBi slopes, left and right sliding windows
+ * and a logit softcap are rejected (fields alibi, window_size_left,
+ * window_size_right, softcap).
+ *
+ * The sparse variant follows the metrale page "AttnV41" (decode_fixed_topk,
+ * decode_prep, decode_body): each token attends the KV rows listed in its
+ * selection, padded with -1 to a fixed launch width topk; a pad adds exactly
+ * zero to the softmax denominator and nothing to the output, so padding the
+ * same valid entries to any width gives bit-identical output.
+ *
+ * Conventions (every call):
+ *   - Every tensor is contiguous row-major. q, k, v and out are bfloat16
+ *     (passed as raw device pointers); sel is int32; the workspace is raw
+ *     bytes. All device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer and the stream. The library allocates and
+ *     frees nothing, performs no host<->device copy and no synchronisation;
+ *     both compute calls only enqueue kernels on `stream` (a hipStream_t, NULL
+ *     for the default stream), so they can be captured into a HIP graph with
+ *     fixed pointers. (Caller-owned, graph-stable buffers and no device-to-host
+ *     validation sync are the conventions of the flashinfer page
+ *     "packed_fused_kda_decode".)
+ *   - Validation fails closed on host-visible arguments and returns a status;
+ *     nothing is thrown across the ABI. Values that live in device memory
+ *     (the selection entries) are caller-owned and are not validated.
+ *   - decode_attn_last_error() returns a thread-local, human-readable message
+ *     for the last failing call on the calling thread.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_ERR_INVALID_ARG = 1, /* bad shape, range, pointer, alignment or plan mismatch */
+  DA_ERR_UNSUPPORTED = 2, /* a feature the kernels do not implement (ALiBi, window, softcap) */
+  DA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than plan.workspace_bytes */
+  DA_ERR_HIP = 4          /* the HIP runtime reported an error (device query or launch) */
+} decode_attn_status;
+
+/*
+ * The problem a plan serves. Host struct; mirrors the fields of the
+ * "DecodeFlashSpec" statement (q/k/v shapes, causal, alibi, windows, softcap,
+ * k_len) plus the fixed launch width of the sparse variant ("AttnV41",
+ * decode_fixed_topk).
+ */
+typedef struct {
+  int32_t batch;        /* B >= 1: query tokens (one per sequence)                        */
+  int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads                            */
+  int32_t num_kv_heads; /* Hkv >= 1                                                       */
+  int32_t head_dim;     /* D: 64 or 128                                                   */
+  int32_t seq_q;        /* Sq: must be 1 (single-token decode)                            */
+  int64_t capacity;     /* rows per (kv batch, kv head) in K and V                        */
+  int64_t max_k_len;    /* largest k_len a call may pass, 1 <= max_k_len <= capacity      */
+  int32_t topk_max;     /* sparse plan: largest launch topk (>= 1); 0 = dense plan        */
+  int32_t kv_batch;     /* sparse: 1 (rows shared by all tokens) or batch; dense: batch
+                           (0 is read as batch)                                           */
+  int32_t causal;       /* accepted and ignored                                           */
+  int32_t has_alibi;    /* nonzero -> DA_ERR_UNSUPPORTED                                  */
+  int64_t window_left;  /* -1 = none; any other value -> DA_ERR_UNSUPPORTED               */
+  int64_t window_right; /* -1 = none; any other value -> DA_ERR_UNSUPPORTED               */
+  int32_t has_softcap;  /* nonzero -> DA_ERR_UNSUPPORTED                                  */
+  int32_t num_cus;      /* compute units to plan for; 0 = query the current HIP device    */
+  int32_t force_splits; /* > 0: dense split count cap (tuning and tests); 0 = heuristic   */
+  int32_t force_chunk;  /* > 0: keys (dense) or selection entries (sparse) per split      */
+} decode_attn_problem;
+
+/*
+ * A plan: plain data, copyable, no device state. Produced by decode_attn_plan
+ * and passed by pointer to every compute call.
+ */
+typedef struct {
+  decode_attn_problem prob; /* the validated problem (kv_batch resolved)               */
+  int32_t group;            /* Hq / Hkv                                                */
+  int32_t num_splits_max;   /* most key splits any call of this plan launches          */
+  int32_t chunk;            /* sparse: selection entries per split (fixed by the plan);
+                               dense: keys per split at max_k_len                      */
+  int32_t num_cus;          /* compute units the plan was made for                      */
+  int32_t kind;             /* 0 dense, 1 sparse                                       */
+  int32_t reserved0;
+  uint64_t workspace_bytes; /* bytes of workspace every call of this plan needs (may be 0) */
+} decode_attn_plan_t;
+
+/*
+ * Validate a problem and choose the split-K decomposition.
+ *   p    host pointer to the problem; out  host pointer that receives the plan.
+ * Returns DA_OK, DA_ERR_INVALID_ARG (shapes/ranges), DA_ERR_UNSUPPORTED (ALiBi,
+ * window, softcap, head_dim other than 64/128, seq_q != 1), or DA_ERR_HIP when
+ * num_cus is 0 and the device query fails. Touches the GPU only for that query.
+ */
+decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_plan_t* out);
+
+/*
+ * Dense decode attention over the live prefix [0, k_len) of the capacity buffers.
+ *   q    [B, Hq, 1, D] bf16            k, v [B, Hkv, capacity, D] bf16
+ *   out  [B, Hq, 1, D] bf16 (written)  softmax_scale  finite f32
+ *   k_len  1 <= k_len <= plan->prob.max_k_len; rows >= k_len are never read
+ *   workspace  device scratch of at least plan->workspace_bytes (may be NULL when
+ *          that is 0); its contents on entry do not matter.
+ * Enqueues one or two kernels on `stream` and returns without waiting.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_WORKSPACE or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void* q,
+                                     const void* k, const void* v, void* out,
+                                     float softmax_scale, int64_t k_len, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * Index-selected sparse decode attention.
+ *   q    [B, Hq, 1, D] bf16           k, v [kv_batch, Hkv, capacity, D] bf16
+ *   sel  [B, topk] int32 (device): token b attends rows sel[b, t] of its KV set
+ *        (set 0 when kv_batch == 1, set b otherwise), for every KV head; entries
+ *        < 0 are pads. Valid entries must lie in [0, k_len): an entry >= k_len is
+ *        a caller error, which the kernel does not report but never reads
+ *        through (it is skipped like a pad). Duplicates count with multiplicity.
+ *   topk 1 <= topk <= plan->prob.topk_max: the launch width (row stride of sel).
+ *   out  [B, Hq, 1, D] bf16 (written). A token with no valid entry gets zeros.
+ *   k_len rows usable by the selection, 1 <= k_len <= capacity.
+ * The split of the selection into chunks is fixed by the plan and does not
+ * depend on topk, so the same valid entries padded to any topk <= topk_max give
+ * bit-identical output.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_WORKSPACE or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void* q,
+                                      const void* k, const void* v, const int32_t* sel,
+                                      int32_t topk, void* out, float softmax_scale,
+                                      int64_t k_len, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * Diagnostics: time the split-K partial kernel (the kernel that streams K and V)
+ * with caller-created HIP events. After this call, every compute call made on
+ * the calling thread records `ev_before` on its stream immediately before
+ * launching its partial kernel and `ev_after` immediately after it, so that
+ * hipEventElapsedTime(ev_before, ev_after) is that kernel's duration. Events
+ * are hipEvent_t handles owned by the caller; passing NULL for both stops the
+ * recording. Returns DA_OK, or DA_ERR_INVALID_ARG if exactly one is NULL.
+ * (Not part of the operation; for benchmarks and profilers.)
+ */
+decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after);
+
+/* Static string naming a status code. */
+const char* decode_attn_status_str(decode_attn_status s);
+
+/* Message for the last failing call on this thread ("" if none). Host memory,
+ * valid until the next call on this thread. */
+const char* decode_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 oracle.
+
+Tolerance (bf16 output): |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise, plus a
+relative L2 error <= 1e-2 and a per-row cosine >= 0.999 (the elementwise bound
+alone would accept an all-zero output at long context, where |out| ~ 0.02).
+Bit-exact: k_len = 1, causal on/off, run-to-run, and the same valid selection
+padded with -1 to any launch width.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def da():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.ensure_built()
+    import decode_attention_05_amd as m
+    m.library()
+    return m
+
+
+def run_dense(da, q, k, v, scale, k_len, max_k_len=None, **plan_kw):
+    import torch
+    B, Hq, _, D = q.shape
+    _, Hkv, cap, _ = k.shape
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, max_k_len or k_len, **plan_kw)
+    dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
+    ws = da.workspace_for(plan)
+    da.decode_attn_dense(plan, dq, dk, dv, out, scale, k_len, ws)
+    torch.cuda.synchronize()
+    return H.from_dev(out), plan
+
+
+def run_sparse(da, q, k, v, sel, scale, k_len=None, topk_max=None, **plan_kw):
+    import torch
+    B, Hq, _, D = q.shape
+    kvb, Hkv, cap, _ = k.shape
+    topk = sel.shape[1]
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, topk_max=topk_max or topk, kv_batch=kvb,
+                               **plan_kw)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
+    ws = da.workspace_for(plan)
+    da.decode_attn_sparse(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev_i32(sel), topk,
+                          out, scale, k_len, ws)
+    torch.cuda.synchronize()
+    return H.from_dev(out), plan
+
+
+def rand(seed, B, Hq, Hkv, D, cap, std=1.0):
+    return W.random_case(seed, B, Hq, Hkv, D, cap, std)
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("name", ["tiny", "gqa", "batch"])
+def test_dense_workload_full_parity(da, name):
+    case, (q, k, v) = H.dense_case_inputs(name)
+    H.log(f"dense workload {name} seed={case.seed} B={case.B} Hq={case.Hq} Hkv={case.Hkv} "
+          f"D={case.D} cap={case.capacity} k_len={case.k_len}")
+    got, plan = run_dense(da, q, k, v, case.scale, case.k_len)
+    ref = oracle.dense(q, k, v, case.scale, case.k_len)
+    H.check_tolerance(got, ref, name)
+
+
+def test_dense_long_context_parity(da):
+    # The long-context workload at its full size (k_len = capacity = 131072),
+    # launched exactly as the benchmark launches it; every output row is checked.
+    case, (q, k, v) = H.dense_case_inputs("long")
+    H.log(f"dense workload long seed={case.seed} k_len={case.k_len}")
+    got, plan = run_dense(da, q, k, v, case.scale, case.k_len)
+    assert plan.num_splits_max > 1
+    ref = oracle.dense(q, k, v, case.scale, case.k_len)
+    H.check_tolerance(got, ref, "long")
+
+
+@pytest.mark.parametrize("name", ["sparse", "sparse_mixed"])
+def test_sparse_workload_full_parity(da, name):
+    case, (q, k, v, sel) = H.sparse_case_inputs(name)
+    H.log(f"sparse workload {name} seed={case.seed} topk={case.topk}")
+    got, _ = run_sparse(da, q, k, v, sel, case.scale, case.rows)
+    ref = oracle.sparse(q, k, v, sel, case.scale, case.rows)
+    H.check_tolerance(got, ref, name)
+
+
+def test_gqa_poison_beyond_k_len_is_never_used(da):
+    case, (q, k, v) = H.dense_case_inputs("gqa")
+    assert (k[:, :, case.k_len:] == W.BF16_NAN).all()
+    got, _ = run_dense(da, q, k, v, case.scale, case.k_len)
+    assert np.isfinite(H.as_f64(got)).all()
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_key_is_bit_exact(da, D):
+    q, k, v = rand(31, 2, 8, 2, D, 64)
+    H.log(f"k_len=1 D={D}")
+    got, _ = run_dense(da, q, k, v, 0.125, 1, max_k_len=64)
+    want = np.repeat(v[:, :, :1, :], 4, axis=1)  # head h reads kv head h // 4
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("k_len", [1, 2, 15, 17, 63, 255, 257, 1000, 4095, 4096])
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_lengths(da, D, k_len):
+    q, k, v = rand(32 + k_len, 2, 8, 4, D, 4096)
+    H.log(f"ragged k_len={k_len} D={D}")
+    got, _ = run_dense(da, q, k, v, 1.0 / math.sqrt(D), k_len, max_k_len=4096)
+    H.check_tolerance(got, oracle.dense(q, k, v, 1.0 / math.sqrt(D), k_len), f"k_len={k_len}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (12, 4), (24, 8), (16, 2), (64, 1),
+                                    (48, 8), (3, 1)])
+def test_group_sizes(da, Hq, Hkv):
+    q, k, v = rand(40 + Hq, 2, Hq, Hkv, 128, 700)
+    H.log(f"group Hq={Hq} Hkv={Hkv}")
+    got, _ = run_dense(da, q, k, v, 0.09, 613)
+    H.check_tolerance(got, oracle.dense(q, k, v, 0.09, 613), f"Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0, 64])
+def test_forced_split_counts(da, splits):
+    q, k, v = rand(50, 2, 16, 2, 128, 3000)
+    H.log(f"force_splits={splits}")
+    got, plan = run_dense(da, q, k, v, 0.1, 2999, force_splits=splits)
+    H.check_tolerance(got, oracle.dense(q, k, v, 0.1, 2999), f"splits={splits}")
+
+
+def test_forced_chunk_tiny(da):
+    q, k, v = rand(51, 1, 8, 1, 64, 100)
+    got, plan = run_dense(da, q, k, v, 0.3, 97, force_chunk=1)   # one key per split
+    assert plan.num_splits_max == 97
+    H.check_tolerance(got, oracle.dense(q, k, v, 0.3, 97), "chunk=1")
+
+
+def test_large_scores_are_stable(da):
+    # Scores in the hundreds: the online softmax must subtract its running max.
+    q, k, v = rand(52, 1, 8, 2, 128, 512, std=4.0)
+    got, _ = run_dense(da, q, k, v, 1.0, 512)
+    H.check_tolerance(got, oracle.dense(q, k, v, 1.0, 512), "large scores")
+
+
+def test_causal_flag_changes_nothing(da):
+    q, k, v = rand(53, 2, 8, 2, 128, 1000)
+    a, _ = run_dense(da, q, k, v, 0.1, 999, causal=False)
+    b, _ = run_dense(da, q, k, v, 0.1, 999, causal=True)
+    assert np.array_equal(a, b)
+
+
+def test_run_to_run_bit_identical(da):
+    case, (q, k, v) = H.dense_case_inputs("gqa")
+    a, _ = run_dense(da, q, k, v, case.scale, case.k_len)
+    b, _ = run_dense(da, q, k, v, case.scale, case.k_len)
+    assert np.array_equal(a, b)
+
+
+def test_plan_reuse_across_k_len(da):
+    # One plan sized for the largest length serves every shorter call.
+    import torch
+    q, k, v = rand(54, 2, 8, 2, 128, 5000)
+    plan = da.decode_attn_plan(2, 8, 2, 128, 5000, 5000)
+    dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+    ws = da.workspace_for(plan)
+    for k_len in (1, 300, 4097, 5000):
+        out = torch.empty((2, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+        da.decode_attn_dense(plan, dq, dk, dv, out, 0.1, k_len, ws)
+        torch.cuda.synchronize()
+        H.check_tolerance(H.from_dev(out), oracle.dense(q, k, v, 0.1, k_len), f"k_len={k_len}")
+
+
+# ------------------------------------------------------------ sparse contract
+
+def test_padding_is_bit_exact(da):
+    # Tokens 1..3 of the mixed selection: the same valid prefix launched with the
+    # narrowest width that holds it, with 2048 and with 4096 gives identical bytes.
+    case, (q, k, v, sel) = H.sparse_case_inputs("sparse_mixed")
+    q = q[1:]
+    sel = sel[1:]
+    n_valid = int((sel >= 0).sum(axis=1).max())
+    assert n_valid == 1465
+    outs = []
+    plan_kw = dict(topk_max=4096)
+    for width in (n_valid, 2048, 4096):
+        H.log(f"padding width={width}")
+        got, _ = run_sparse(da, q, k, v, W.repad(sel, width), case.scale, case.rows, **plan_kw)
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    H.check_tolerance(outs[0], oracle.sparse(q, k, v, sel, case.scale), "padding")
+
+
+def test_interleaved_pads_within_tolerance(da):
+    case, (q, k, v, sel) = H.sparse_case_inputs("sparse_mixed")
+    inter = np.full((sel.shape[0], 4096), -1, np.int32)
+    inter[:, ::2] = sel
+    got, _ = run_sparse(da, q, k, v, inter, case.scale, case.rows)
+    H.check_tolerance(got, oracle.sparse(q, k, v, inter, case.scale), "interleaved")
+
+
+def test_all_pad_token_gives_zeros(da):
+    q, k, v = rand(60, 1, 16, 1, 128, 300)
+    q = np.repeat(q, 2, axis=0)
+    sel = np.full((2, 64), -1, np.int32)
+    sel[1, :10] = np.arange(10)
+    got, _ = run_sparse(da, q, k, v, sel, 0.1)
+    assert np.array_equal(got[0], np.zeros_like(got[0]))
+    H.check_tolerance(got, oracle.sparse(q, k, v, sel, 0.1), "all-pad")
+
+
+def test_sparse_per_token_kv_sets(da):
+    B = 3
+    q, k, v = rand(61, B, 8, 2, 128, 400)   # kv_batch == B
+    rng = np.random.Generator(np.random.PCG64(62))
+    sel = np.stack([rng.choice(400, 100, replace=False) for _ in range(B)]).astype(np.int32)
+    sel = W.repad(sel, 128)
+    got, _ = run_sparse(da, q, k, v, sel, 0.1)
+    H.check_tolerance(got, oracle.sparse(q, k, v, sel, 0.1), "kv_batch=B")
+
+
+def test_sparse_duplicates_and_out_of_range_entries(da):
+    # Duplicates count twice; entries >= k_len are never read (skipped like pads).
+    q, k, v = rand(63, 2, 8, 1, 64, 256)
+    sel = np.array([[5, 5, 9, -1, 200, 7], [1, 2, 3, 250, 251, -1]], np.int32)
+    got, _ = run_sparse(da, q, k, v, sel, 0.2, k_len=256)
+    H.check_tolerance(got, oracle.sparse(q, k, v, sel, 0.2, 256), "duplicates")
+    skipped = np.where(sel >= 240, -1, sel)
+    got2, _ = run_sparse(da, q, k, v, sel, 0.2, k_len=240)
+    H.check_tolerance(got2, oracle.sparse(q, k, v, skipped, 0.2, 240), "out of range")
+
+
+@pytest.mark.parametrize("Hkv", [1, 4])
+def test_dense_equals_sparse_over_prefix(da, Hkv):
+    B, k_len = 2, 777
+    q, k, v = rand(64, B, 16, Hkv, 128, 1024)
+    sel = W.repad(np.tile(np.arange(k_len, dtype=np.int32), (B, 1)), 1024)
+    d, _ = run_dense(da, q, k, v, 0.1, k_len)
+    s, _ = run_sparse(da, q, k, v, sel, 0.1, k_len=k_len)
+    ref = oracle.dense(q, k, v, 0.1, k_len)
+    H.check_tolerance(d, ref, "dense")
+    H.check_tolerance(s, ref, "sparse")
+
+
+def test_binding_rejects_mismatched_tensors(da):
+    import torch
+    plan = da.decode_attn_plan(2, 8, 2, 128, 100, 100)
+    q = torch.empty((2, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((2, 2, 99, 128), dtype=torch.bfloat16, device="cuda")  # one row short
+    out = torch.empty_like(q)
+    with pytest.raises(ValueError):
+        da.decode_attn_dense(plan, q, kv, kv, out, 0.1, 50, da.workspace_for(plan))
+    with pytest.raises(TypeError):
+        da.decode_attn_dense(plan, q.float(), kv, kv, out, 0.1, 50, da.workspace_for(plan))

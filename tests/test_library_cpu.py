@@ -1,0 +1,169 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every declared symbol,
+plans every workload, and fails closed on every invalid argument -- all without
+a GPU (no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.helpers import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def da():
+    ensure_built()
+    import decode_attention_05_amd as m
+    m.library()
+    return m
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(decode_attn_\w+)\s*\(", text))
+    return names
+
+
+def test_exports_every_declared_symbol(da):
+    names = declared_functions()
+    assert {"decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
+            "decode_attn_status_str", "decode_attn_last_error"} <= names
+    lib = ctypes.CDLL(da.library_path)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(da.EXPORTED_SYMBOLS) <= names
+
+
+def test_struct_layout_matches_header(da, tmp_path):
+    # Compile a probe against the header with the system C compiler and compare
+    # every field offset and both struct sizes with the binding's ctypes mirror.
+    probe = tmp_path / "probe.c"
+    fields_p = [f for f, _ in da.Problem._fields_]
+    fields_l = [f for f, _ in da.Plan._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "decode_attn.h"',
+             "int main(void) {",
+             '  printf("%zu\\n", sizeof(decode_attn_problem));',
+             '  printf("%zu\\n", sizeof(decode_attn_plan_t));']
+    lines += [f'  printf("%zu\\n", offsetof(decode_attn_problem, {f}));' for f in fields_p]
+    lines += [f'  printf("%zu\\n", offsetof(decode_attn_plan_t, {f}));' for f in fields_l]
+    lines += ["  return 0;", "}"]
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    import subprocess
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(probe),
+                           "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(da.Problem), ctypes.sizeof(da.Plan)]
+    want += [getattr(da.Problem, f).offset for f in fields_p]
+    want += [getattr(da.Plan, f).offset for f in fields_l]
+    assert got == want
+
+
+def test_status_strings(da):
+    assert da.decode_attn_status_str(0) == "DA_OK"
+    assert da.decode_attn_status_str(2) == "DA_ERR_UNSUPPORTED"
+    assert da.decode_attn_status_str(99) == "DA_ERR_UNKNOWN"
+
+
+def plan(da, **kw):
+    base = dict(batch=4, num_q_heads=64, num_kv_heads=8, head_dim=128, capacity=4096, num_cus=256)
+    base.update(kw)
+    return da.decode_attn_plan(**base)
+
+
+@pytest.mark.parametrize("field,value", [("has_alibi", True), ("window_left", 128),
+                                         ("window_right", 0), ("has_softcap", True),
+                                         ("seq_q", 2), ("head_dim", 96)])
+def test_rejected_features(da, field, value):
+    with pytest.raises(da.DecodeAttnError) as ei:
+        plan(da, **{field: value})
+    assert ei.value.status == 2  # DA_ERR_UNSUPPORTED
+    name = field if field not in ("has_alibi", "has_softcap") else field[4:]
+    assert name in str(ei.value)
+
+
+def test_causal_is_accepted(da):
+    a, b = plan(da, causal=True), plan(da, causal=False)
+    assert (a.num_splits_max, a.chunk, a.workspace_bytes) == (b.num_splits_max, b.chunk,
+                                                             b.workspace_bytes)
+
+
+@pytest.mark.parametrize("kw", [dict(num_q_heads=12, num_kv_heads=8), dict(batch=0),
+                                dict(num_kv_heads=0), dict(capacity=0),
+                                dict(max_k_len=0), dict(max_k_len=4097),
+                                dict(topk_max=-1), dict(topk_max=16, kv_batch=2),
+                                dict(kv_batch=3), dict(num_cus=-1), dict(force_splits=-2)])
+def test_invalid_problems(da, kw):
+    with pytest.raises(da.DecodeAttnError) as ei:
+        plan(da, **kw)
+    assert ei.value.status == 1
+
+
+def test_dense_plans_for_the_workloads(da):
+    # split counts with 256 compute units: enough workgroups to fill the chip,
+    # never fewer than 256 keys per split
+    tiny = da.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256)
+    assert tiny.num_splits_max == 2 and tiny.workspace_bytes == 1 * 8 * 2 * 66 * 4
+    gqa = da.decode_attn_plan(8, 32, 8, 128, 8192, 4096, num_cus=256)
+    assert gqa.num_splits_max == 16 and gqa.chunk == 256
+    long = da.decode_attn_plan(4, 64, 8, 128, 131072, 131072, num_cus=256)
+    assert long.num_splits_max == 32 and long.chunk == 4096
+    assert long.workspace_bytes == 4 * 64 * 32 * 130 * 4
+    batch = da.decode_attn_plan(128, 32, 8, 128, 2048, 1537, num_cus=256)
+    assert batch.num_splits_max == 1 and batch.workspace_bytes == 0
+
+
+def test_sparse_plan_chunk_is_independent_of_call(da):
+    p = da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=2048, kv_batch=1, num_cus=256)
+    assert p.sparse and p.chunk % 16 == 0
+    assert p.num_splits_max == -(-2048 // p.chunk)
+    q = da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=4096, kv_batch=1, num_cus=256,
+                            force_chunk=p.chunk)
+    assert q.chunk == p.chunk
+
+
+def test_compute_calls_fail_closed_before_any_launch(da):
+    lib = da.library()
+    P = plan(da)
+    fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails first
+    ws = ctypes.c_void_p(0x20000)
+    call = lambda *a: lib.decode_attn_dense(ctypes.byref(P), *a)  # noqa: E731
+    # NULL pointer
+    assert call(None, fake, fake, fake, 0.1, 10, ws, P.workspace_bytes, None) == 1
+    # misaligned
+    assert call(ctypes.c_void_p(0x10002), fake, fake, fake, 0.1, 10, ws, P.workspace_bytes,
+                None) == 1
+    # non-finite scale
+    assert call(fake, fake, fake, fake, float("nan"), 10, ws, P.workspace_bytes, None) == 1
+    assert call(fake, fake, fake, fake, float("inf"), 10, ws, P.workspace_bytes, None) == 1
+    # k_len outside [1, max_k_len]
+    assert call(fake, fake, fake, fake, 0.1, 0, ws, P.workspace_bytes, None) == 1
+    assert call(fake, fake, fake, fake, 0.1, 4097, ws, P.workspace_bytes, None) == 1
+    assert "k_len" in da.decode_attn_last_error()
+    # workspace missing or too small
+    assert P.workspace_bytes > 0
+    assert call(fake, fake, fake, fake, 0.1, 10, None, P.workspace_bytes, None) == 3
+    assert call(fake, fake, fake, fake, 0.1, 10, ws, P.workspace_bytes - 1, None) == 3
+    # a sparse plan handed to the dense call
+    S = da.decode_attn_plan(2, 8, 1, 128, 1000, topk_max=64, kv_batch=1, num_cus=256)
+    assert lib.decode_attn_dense(ctypes.byref(S), fake, fake, fake, fake, 0.1, 10, ws,
+                                 S.workspace_bytes, None) == 1
+    # sparse: topk outside [1, topk_max], k_len outside [1, capacity], misaligned sel
+    scall = lambda sel, topk, k_len: lib.decode_attn_sparse(  # noqa: E731
+        ctypes.byref(S), fake, fake, fake, sel, topk, fake, 0.1, k_len, ws, S.workspace_bytes, None)
+    assert scall(fake, 0, 1000) == 1
+    assert scall(fake, 65, 1000) == 1
+    assert scall(fake, 64, 1001) == 1
+    assert scall(fake, 64, 0) == 1
+    assert scall(None, 64, 1000) == 1
+    assert scall(ctypes.c_void_p(0x10002), 64, 1000) == 1
+    # the dense plan handed to the sparse call
+    assert lib.decode_attn_sparse(ctypes.byref(P), fake, fake, fake, fake, 8, fake, 0.1, 10, ws,
+                                  P.workspace_bytes, None) == 1

@@ -31,11 +31,7 @@ def f(x):
 
 
 def rand_case(seed, B, Hq, Hkv, D, cap, std=1.0):
-    rng = np.random.Generator(np.random.PCG64(seed))
-    q = W.normal_bf16(rng, (B, Hq, 1, D), std)
-    k = W.normal_bf16(rng, (B, Hkv, cap, D), std)
-    v = W.normal_bf16(rng, (B, Hkv, cap, D), std)
-    return q, k, v
+    return W.random_case(seed, B, Hq, Hkv, D, cap, std)
 
 
 # ---------------------------------------------------------------- fixtures
@@ -118,8 +114,7 @@ def test_two_keys_logistic(s0, s1):
     k = np.zeros((1, 1, 2, D), np.float32)
     q[0, 0, 0, 0] = 1.0
     k[0, 0, 0, 0], k[0, 0, 1, 0] = s0, s1
-    rng = np.random.Generator(np.random.PCG64(14))
-    v = W.normal_bf16(rng, (1, 1, 2, D))
+    v = W.normal_bf16(np.random.SeedSequence(14), (1, 1, 2, D))
     assert np.array_equal(f(bits(k)), k)        # the chosen scores are bf16-exact
     out = oracle.dense(bits(q), bits(k), v, 1.0, 2)[0, 0, 0]
     sig = lambda x: 1.0 / (1.0 + math.exp(-x))  # noqa: E731
@@ -237,9 +232,7 @@ def test_duplicates_count_with_multiplicity():
     # zero scores, the output is (2 v_a + v_b) / 3.
     D = 64
     q = np.zeros((1, 2, 1, D), np.uint16)
-    rng = np.random.Generator(np.random.PCG64(24))
-    k = W.normal_bf16(rng, (1, 1, 8, D))
-    v = W.normal_bf16(rng, (1, 1, 8, D))
+    _, k, v = W.random_case(24, 1, 1, 1, D, 8)
     out = oracle.sparse(q, k, v, np.array([[5, 2, 5, -1]], np.int32), 1.0)
     ref = (2 * f(v[0, 0, 5]) + f(v[0, 0, 2])) / 3
     np.testing.assert_allclose(out[0, 0, 0], ref, rtol=0, atol=1e-13)

@@ -5,8 +5,10 @@ draws inputs and nothing else: it holds none of the attention arithmetic.
 
 Values are drawn with numpy's PCG64 generator as float32 standard normals,
 multiplied by a standard deviation, and rounded to bfloat16 with IEEE
-round-to-nearest-even. Arrays are drawn in the order q, K, V, then the
-selection. Every array is returned as raw bfloat16 bit patterns (uint16) so
+round-to-nearest-even. The workload seed is split (numpy SeedSequence) into
+one child each for q, K, V and the selection, and every array is drawn in
+fixed blocks from its own children, so large arrays fill in parallel and the
+bits depend only on seed and shape. Every array is returned as raw bfloat16 bit patterns (uint16) so
 that both sides see exactly the same bits.
 
 Workloads (shapes follow the problem statement of the fuel-dispatch page
@@ -26,7 +28,9 @@ follows the metrale page "AttnV41", decode_fixed_topk and decode_prep):
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -50,12 +54,48 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
     return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
-    """float32 N(0, std^2) draws rounded to bfloat16 bits."""
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    return f32_to_bf16_bits(x)
+BLOCK = 1 << 20  # elements per independently seeded block
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal_bf16(seed: np.random.SeedSequence, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws rounded to bfloat16 bits.
+
+    The flat array is cut into blocks of BLOCK elements; block i is drawn from
+    the i-th child of ``seed`` (``seed.spawn``), so the result depends only on
+    the seed and the shape, never on how many threads fill it.
+    """
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    nblocks = max(1, -(-n // BLOCK))
+    children = seed.spawn(nblocks)
+
+    def fill(i):
+        lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+        rng = np.random.Generator(np.random.PCG64(children[i]))
+        x = rng.standard_normal(size=hi - lo, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    if nblocks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nblocks)))
+    return out.reshape(shape)
+
+
+def seeds(seed: int, n: int = 4):
+    """Independent child seeds for q, K, V and the selection, in that order."""
+    return np.random.SeedSequence(seed).spawn(n)
 
 
 @dataclass
@@ -138,10 +178,10 @@ SPARSE_CASES = {
 
 def dense_inputs(case: DenseCase, seed: int | None = None):
     """q [B,Hq,1,D], k and v [B,Hkv,capacity,D] as bfloat16 bits."""
-    rng = np.random.Generator(np.random.PCG64(case.seed if seed is None else seed))
-    q = normal_bf16(rng, (case.B, case.Hq, 1, case.D), case.std)
-    k = normal_bf16(rng, (case.B, case.Hkv, case.capacity, case.D), case.std)
-    v = normal_bf16(rng, (case.B, case.Hkv, case.capacity, case.D), case.std)
+    sq, sk, sv, _ = seeds(case.seed if seed is None else seed)
+    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    k = normal_bf16(sk, (case.B, case.Hkv, case.capacity, case.D), case.std)
+    v = normal_bf16(sv, (case.B, case.Hkv, case.capacity, case.D), case.std)
     if case.poison and case.k_len < case.capacity:
         k[:, :, case.k_len:, :] = BF16_NAN
         v[:, :, case.k_len:, :] = BF16_NAN
@@ -170,12 +210,20 @@ def selection(rng: np.random.Generator, B: int, rows: int, topk: int, window: in
 
 def sparse_inputs(case: SparseCase, seed: int | None = None):
     """q [B,Hq,1,D]; k, v [kv_batch,Hkv,rows,D]; sel [B,topk] int32."""
-    rng = np.random.Generator(np.random.PCG64(case.seed if seed is None else seed))
-    q = normal_bf16(rng, (case.B, case.Hq, 1, case.D), case.std)
-    k = normal_bf16(rng, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
-    v = normal_bf16(rng, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
-    sel = selection(rng, case.B, case.rows, case.topk, case.window, case.counts)
+    sq, sk, sv, ss = seeds(case.seed if seed is None else seed)
+    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    k = normal_bf16(sk, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
+    v = normal_bf16(sv, (case.kv_batch, case.Hkv, case.rows, case.D), case.std)
+    sel = selection(np.random.Generator(np.random.PCG64(ss)), case.B, case.rows, case.topk,
+                    case.window, case.counts)
     return q, k, v, sel
+
+
+def random_case(seed: int, B: int, Hq: int, Hkv: int, D: int, cap: int, std: float = 1.0):
+    """Small seeded q, K, V (bfloat16 bits) of arbitrary shape, for tests."""
+    sq, sk, sv, _ = seeds(seed)
+    return (normal_bf16(sq, (B, Hq, 1, D), std), normal_bf16(sk, (B, Hkv, cap, D), std),
+            normal_bf16(sv, (B, Hkv, cap, D), std))
 
 
 def repad(sel: np.ndarray, topk: int) -> np.ndarray:
