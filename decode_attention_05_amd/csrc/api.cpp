@@ -87,8 +87,10 @@ constexpr int kMinChunk = 256;
 constexpr int kKeyAlign = 16;
 constexpr int kMaxSplits = 1 << 16;
 
+// Query heads one workgroup serves: the largest divisor of the group size that
+// fits the 16 columns of one MFMA tile.
 int heads_per_wg(int G) {
-  for (int gt : {8, 4, 2, 1})
+  for (int gt = 16; gt > 1; --gt)
     if (G % gt == 0) return gt;
   return 1;
 }

@@ -1,26 +1,35 @@
-// kernels.hip -- split-K decode attention kernels for gfx950.
+// kernels.hip -- split-K decode attention kernels for gfx950 (CDNA4).
 //
 // The operation is softmax(scale * q . K^T) V for one query token per sequence
 // (fuel-dispatch page "DecodeFlashSpec": q [B, Hq, 1, D] against the capacity
-// buffers [B, Hkv, capacity, D] over the live prefix [0, k_len)), and its
-// index-selected form (metrale page "AttnV41", decode_fixed_topk: rows named
-// by a -1-padded selection, a pad adding exactly zero).
+// buffers [B, Hkv, capacity, D] over the live prefix [0, k_len), grouped-query
+// heads), and its index-selected form (metrale page "AttnV41",
+// decode_fixed_topk: rows named by a -1-padded selection, a pad adding exactly
+// zero).
 //
-// Decomposition (split-K over keys, a.k.a. flash-decoding): one workgroup owns
-// a (batch, kv head, head tile, split) and streams its chunk of keys once.
-//   - The GQA query rows of the head tile are staged through LDS as fp32,
-//     pre-multiplied by scale * log2(e) so the softmax runs in base 2.
-//   - A KV row of D bf16 is read by D/8 lanes with one 16-byte load each (a
-//     "row group"); a wave covers 64/(D/8) rows per load instruction, so every
-//     load instruction of a wave reads 1 KiB of contiguous KV memory.
-//   - Each row group keeps its own online-softmax state (running max m, sum l,
-//     unnormalised output o) over the rows it visits. q.k partial dot products
-//     are summed over the row group with a DPP butterfly.
-//   - At the end the row groups of the workgroup are merged (in a fixed order:
-//     deterministic), and the workgroup either writes the normalised bf16
-//     output (one split) or its (o, m, l) partial for the combine kernel.
-// Pads and tail rows are never loaded: their score is -inf, their weight +0
-// and their value -0, so they leave every accumulator bit-for-bit unchanged.
+// Decomposition (split-K over keys): one workgroup owns a (batch, kv head,
+// head tile, split); each of its four waves streams every fourth 32-key tile
+// of the split and keeps its own base-2 online-softmax state; the waves are
+// merged at the end, and a second kernel merges the splits (log-sum-exp).
+//
+// Per 32-key tile, for the (up to 16) query heads of the head tile:
+//   S^T[32 keys x 16 heads] = K_tile . Q^T  two v_mfma_f32_16x16x32_bf16 chains over D.
+//       K is loaded from HBM straight into the A-operand layout: lane l holds
+//       16 bytes of key row (l % 16); a wave instruction reads 64 contiguous
+//       bytes of each of 16 rows, and the D/64 instructions cover the rows.
+//   softmax: scores * scale * log2(e); per-head running max m (wave-reduced),
+//       weights p = 2^(s - m) rounded to bf16 (the same rounded weights feed the
+//       denominator l and the output), rescale of l and O by 2^(m_old - m_new).
+//   O^T[D x 16 heads] += V_tile^T . P^T   D/16 MFMAs, one per 16-wide d tile.
+//       V is staged through LDS (coalesced 1 KiB-per-instruction loads, XOR-
+//       swizzled 16-byte chunks) and read back transposed with
+//       ds_read_b64_tr_b16, which hands each lane 4 keys of one d column.
+// The next tile's K and V loads are issued before the current tile is
+// processed (register double buffering), so every wave keeps 16 KiB in flight.
+//
+// Keys outside the split, past k_len, or (sparse) pads and out-of-range
+// entries are never loaded: their K and V rows are zeros and their score is
+// -inf, so their weight is exactly 0. A tile with no valid key is skipped.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,219 +37,282 @@ namespace da {
 
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kUnroll = 2;     // rows per row group per iteration
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileKeys = 32;
 
-template <int D, int GT, bool SPARSE>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialLaunch a) {
-  constexpr int LPR = D / 8;     // lanes per KV row (16 bytes each)
-  constexpr int RPW = 64 / LPR;  // rows per wave per load instruction
-  constexpr int NRG = 4 * RPW;   // row groups per workgroup
-  constexpr int STEP = NRG * kUnroll;
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ shortx4 lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (shortx4 __attribute__((address_space(3)))*)(p));
+}
+
+template <int D>
+struct Geometry {
+  static constexpr int ROWB = D * 2;                 // bytes per KV row
+  static constexpr int RU4 = D / 8;                  // 16-byte chunks per row
+  static constexpr int NC = D / 32;                  // k-chunks of the q.k contraction
+  static constexpr int NDT = D / 16;                 // 16-wide d tiles of the output
+  static constexpr int VLD = kTileKeys * RU4 / 64;   // V loads per lane per tile
+  static constexpr int SWZ = (D == 128) ? 7 : 3;     // key bits used by the LDS swizzle
+  static constexpr int VTILE = kTileKeys * ROWB;     // LDS bytes per wave tile
+  static constexpr int OSTRIDE = D + 4;              // floats per head row of the merge area
+  static constexpr int MERGE = kWaves * 16 * OSTRIDE * 4;
+  static constexpr int LDS = (kWaves * VTILE > MERGE ? kWaves * VTILE : MERGE);
+};
+
+// Physical LDS byte offset of 16-byte chunk `chunk` of key row `key` in a V tile.
+template <int D>
+__device__ __forceinline__ int v_off(int key, int chunk) {
+  using Gm = Geometry<D>;
+  return key * Gm::ROWB + ((chunk ^ (2 * (key & Gm::SWZ))) << 4);
+}
+
+template <int D>
+struct TileRegs {
+  uint4 k[2][Geometry<D>::NC];   // A operands: key rows (lane % 16) of the two 16-key halves
+  uint4 v[Geometry<D>::VLD];     // V tile in natural order, destined for LDS
+  uint32_t mask;                 // bit i: key i of the tile is valid
+};
+
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
+  using Gm = Geometry<D>;
+  constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int rg = wave * RPW + lane / LPR;
-  const int sub = lane % LPR;
+  const int g = lane >> 4;   // lane group: which 8 bf16 of a 32-wide k slice
+  const int r16 = lane & 15; // A-operand row / C-operand column
 
   // Workgroup coordinates: split fastest, then head tile, then (b, kv head).
-  const int tiles = a.G / GT;
+  const int GT = a.heads_per_wg;
+  const int tiles_h = a.G / GT;
   int wg = blockIdx.x;
   const int s = wg % a.S;
   wg /= a.S;
-  const int ht = wg % tiles;
-  const int bh = wg / tiles;
+  const int ht = wg % tiles_h;
+  const int bh = wg / tiles_h;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int h0 = hkv * a.G + ht * GT;  // first query head of this tile
 
-  __shared__ float q_lds[GT][D];
-  __shared__ float o_lds[4][GT][D];
-  __shared__ float m_lds[4][GT];
-  __shared__ float l_lds[4][GT];
-
-  for (int i = tid; i < GT * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    const uint16_t raw = a.q[((int64_t)b * a.Hq + h0 + g) * D + d];
-    q_lds[g][d] = __uint_as_float((uint32_t)raw << 16) * a.qscale;
-  }
-  __syncthreads();
-
-  float qr[GT][8];
+  // B operand of S^T = K Q^T: lane holds q[h0 + r16][8 (4c + g) .. + 7].
+  bf16x8 qop[NC];
+  {
+    const bool hv = r16 < GT;
+    const uint4* qrow =
+        reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + h0 + (hv ? r16 : 0)) * D);
 #pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qr[g][e] = q_lds[g][sub * 8 + e];
-
-  float m[GT], l[GT], o[GT][8];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    for (int c = 0; c < NC; ++c)
+      qop[c] = as_bf16x8(hv ? qrow[4 * c + g] : make_uint4(0u, 0u, 0u, 0u));
   }
 
   const int bk = SPARSE ? (a.kv_batch == 1 ? 0 : b) : b;
-  const int64_t kv_off = ((int64_t)bk * a.Hkv + hkv) * a.capacity * D + sub * 8;
-  const uint4* __restrict__ kp = reinterpret_cast<const uint4*>(a.k + kv_off);
-  const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(a.v + kv_off);
-  constexpr int ROW_U4 = D / 8;  // uint4 per KV row
+  const int64_t kv_base = ((int64_t)bk * a.Hkv + hkv) * a.capacity * D;
+  const uint4* __restrict__ kp = reinterpret_cast<const uint4*>(a.k + kv_base);
+  const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(a.v + kv_base);
 
-  // Key range of this split: rows [j0, j1) (dense) or selection entries [j0, j1).
+  // This split: keys (dense) or selection entries (sparse) [j0, j1).
   const int64_t j0 = (int64_t)s * a.chunk;
   const int64_t j_end = SPARSE ? (int64_t)a.topk : a.k_len;
   const int64_t j1 = (j0 + a.chunk < j_end) ? j0 + a.chunk : j_end;
+  const int ntiles = (j1 > j0) ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
   const int32_t* sel_row = SPARSE ? a.sel + (int64_t)b * a.topk : nullptr;
 
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-  const uint4 negzero4 = make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u);
+  unsigned char* vt = lds + wave * Gm::VTILE;  // this wave's V tile
 
-  for (int64_t base = j0; base < j1; base += STEP) {
-    uint4 kr[kUnroll], vr[kUnroll];
-    bool valid[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = base + rg + NRG * u;
-      int64_t row = j;
-      bool ok = j < j1;
-      if constexpr (SPARSE) {
-        const int32_t r = ok ? sel_row[j] : -1;
-        ok = r >= 0 && (int64_t)r < a.k_len;
-        row = r;
-      }
-      valid[u] = ok;
-      if (ok) {
-        kr[u] = kp[row * ROW_U4];
-        vr[u] = vp[row * ROW_U4];
-      } else {
-        kr[u] = zero4;
-        vr[u] = negzero4;  // -0: adding p * (-0) leaves any accumulator unchanged
-      }
+  // Issue the loads of tile `tau` (tile index within the split) into R.
+  auto load_tile = [&](TileRegs<D>& R, int tau) {
+    const int64_t kt = j0 + (int64_t)tau * kTileKeys;
+    int row_lane = -1;  // sparse: row of key (lane & 31) of the tile
+    if constexpr (SPARSE) {
+      const int64_t t = kt + (lane & 31);
+      const int32_t r = (tau < ntiles && t < j1) ? sel_row[t] : -1;
+      row_lane = (r >= 0 && (int64_t)r < a.k_len) ? (int)r : -1;
+      R.mask = (uint32_t)__ballot(row_lane >= 0);
+    } else {
+      const int64_t n = (tau < ntiles) ? j1 - kt : 0;
+      R.mask = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
     }
-
-    float sc[kUnroll][GT];
-    float vf[kUnroll][8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float kf[8];
-      unpack8(kr[u], kf);
-      unpack8(vr[u], vf[u]);
+    for (int sb = 0; sb < 2; ++sb) {
+      const int slot = 16 * sb + r16;
+      int64_t row;
+      if constexpr (SPARSE) row = __shfl(row_lane, slot);
+      else row = ((R.mask >> slot) & 1u) ? kt + slot : -1;
 #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p = fmaf(qr[g][e], kf[e], p);
-        p = group_sum<LPR>(p);
-        sc[u][g] = valid[u] ? p : kNegInf;
-      }
+      for (int c = 0; c < NC; ++c)
+        R.k[sb][c] = row >= 0 ? kp[row * RU4 + 4 * c + g] : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      const int slot = idx / RU4, chunk = idx % RU4;
+      int64_t row;
+      if constexpr (SPARSE) row = __shfl(row_lane, slot);
+      else row = ((R.mask >> slot) & 1u) ? kt + slot : -1;
+      R.v[r] = row >= 0 ? vp[row * RU4 + chunk] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
 
+  floatx4 O[NDT];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float mb = m[g];
+  for (int dt = 0; dt < NDT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;  // running max (base 2) of head r16, same in every lane group
+  float l = 0.f;      // this lane's share of the denominator of head r16
+  const float qscale = a.qscale;
+
+  auto process_tile = [&](const TileRegs<D>& R) {
+    const uint32_t mask = R.mask;
+    if (mask == 0u) return;  // nothing valid: the state is left untouched
+    // V tile -> LDS (swizzled), for the transposed reads below.
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) mb = fmaxf(mb, sc[u][g]);
-      if (mb == kNegInf) continue;  // nothing valid seen yet by this row group
-      const float alpha = exp2_fast(m[g] - mb);
-      float p[kUnroll];
-      float ps = 0.f;
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) = R.v[r];
+    }
+    // S^T halves: keys 4g+i (first) and 16+4g+i (second) for head r16.
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        p[u] = exp2_fast(sc[u][g] - mb);
-        ps += p[u];
-      }
-      l[g] = l[g] * alpha + ps;
+    for (int c = 0; c < NC; ++c) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[0][c]), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[1][c]), qop[c], s1, 0, 0, 0);
+    }
+    float sc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = o[g][e] * alpha;
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
+      sc[i] = ((mask >> k0) & 1u) ? s0[i] * qscale : kNegInf;
+      sc[4 + i] = ((mask >> k1) & 1u) ? s1[i] * qscale : kNegInf;
+    }
+    float mx = sc[0];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
-        o[g][e] = acc;
-      }
-      m[g] = mb;
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);  // finite: the tile holds a valid key
+    const float alpha = exp2_fast(m - m_new);
+    uint32_t pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = pack_bf16(exp2_fast(sc[2 * i] - m_new), exp2_fast(sc[2 * i + 1] - m_new));
+      psum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xffff0000u);
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    // O^T[d tile] = alpha * O^T + V^T P^T. Transposed V reads: lane (g, j = r16)
+    // addresses key 4g + (j >> 2) (+16 for the second half), d = 16 dt + 4 (j & 3);
+    // it receives V[4g + e][16 dt + j] for e = 0..3 (+16), the keys of its P slots.
+    const int jk = 4 * g + (r16 >> 2);
+    const int q4 = r16 & 3;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int chunk = 2 * dt + (q4 >> 1);
+      const int sub = (q4 & 1) * 8;
+      const shortx4 lo = lds_read_tr(vt + v_off<D>(jk, chunk) + sub);
+      const shortx4 hi = lds_read_tr(vt + v_off<D>(16 + jk, chunk) + sub);
+      const bf16x8 vop = __builtin_bit_cast(
+          bf16x8, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                             __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))));
+      O[dt] *= alpha;
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, O[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  };
+
+  // Wave `wave` takes tiles wave, wave + 4, ...; the next tile's loads are in
+  // flight while the current one is processed.
+  {
+    TileRegs<D> A, B;
+    int tau = wave;
+    load_tile(A, tau);
+    while (tau < ntiles) {
+      load_tile(B, tau + kWaves);
+      process_tile(A);
+      tau += kWaves;
+      if (tau >= ntiles) break;
+      load_tile(A, tau + kWaves);
+      process_tile(B);
+      tau += kWaves;
     }
   }
 
-  // Merge the row groups of each wave (lanes that hold the same d slice).
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      float oo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oo[e] = __shfl_xor(o[g][e], off);
-      if (mo == kNegInf) continue;  // partner empty: keep ours
-      if (m[g] == kNegInf) {        // we are empty: take the partner's
-        m[g] = mo;
-        l[g] = lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = oo[e];
-        continue;
-      }
-      const float M = fmaxf(m[g], mo);
-      const float wa = exp2_fast(m[g] - M), wb = exp2_fast(mo - M);
-      l[g] = l[g] * wa + lo * wb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = o[g][e] * wa + oo[e] * wb;
-      m[g] = M;
-    }
-  }
+  // Denominator of head r16 over the four lane groups.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
 
-  // Row group 0 of every wave publishes the wave's state.
-  if (lane < LPR) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o_lds[wave][g][sub * 8 + e] = o[g][e];
-      if (sub == 0) {
-        m_lds[wave][g] = m[g];
-        l_lds[wave][g] = l[g];
-      }
-    }
+  __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
+  float* mo = reinterpret_cast<float*>(lds);
+  if (g == 0) {
+    mrg_m[wave][r16] = m;
+    mrg_l[wave][r16] = l;
   }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    *reinterpret_cast<floatx4*>(mo + (wave * 16 + r16) * Gm::OSTRIDE + 16 * dt + 4 * g) = O[dt];
   __syncthreads();
 
-  // Merge the four waves in order 0..3 and emit: thread t owns head t / LPR and
-  // the 8 values at d = (t % LPR) * 8.
-  if (tid < GT * LPR) {
-    const int g = tid / LPR, d0 = (tid % LPR) * 8;
-    float M = kNegInf, L = 0.f, acc[8];
+  // Merge the waves in order 0..3. Thread t owns head t / 16 and D/16 values.
+  constexpr int PER = D / 16;
+  const int hh = tid >> 4, d0 = (tid & 15) * PER;
+  if (hh < GT) {
+    float M = kNegInf, L = 0.f, acc[PER];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = m_lds[w][g];
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = mrg_m[w][hh];
       if (mw == kNegInf) continue;
+      const float* src = mo + (w * 16 + hh) * Gm::OSTRIDE + d0;
       if (M == kNegInf) {
         M = mw;
-        L = l_lds[w][g];
+        L = mrg_l[w][hh];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = o_lds[w][g][d0 + e];
+        for (int e = 0; e < PER; ++e) acc[e] = src[e];
         continue;
       }
       const float Mn = fmaxf(M, mw);
       const float wa = exp2_fast(M - Mn), wb = exp2_fast(mw - Mn);
-      L = L * wa + l_lds[w][g] * wb;
+      L = L * wa + mrg_l[w][hh] * wb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * wa + o_lds[w][g][d0 + e] * wb;
+      for (int e = 0; e < PER; ++e) acc[e] = acc[e] * wa + src[e] * wb;
       M = Mn;
     }
-    const int64_t row = (int64_t)b * a.Hq + h0 + g;
+    const int64_t row = (int64_t)b * a.Hq + h0 + hh;
     if (a.S == 1) {
       const float inv = (L > 0.f) ? 1.f / L : 0.f;
-      uint4 r;
-      r.x = pack2_bf16(acc[0] * inv, acc[1] * inv);
-      r.y = pack2_bf16(acc[2] * inv, acc[3] * inv);
-      r.z = pack2_bf16(acc[4] * inv, acc[5] * inv);
-      r.w = pack2_bf16(acc[6] * inv, acc[7] * inv);
-      *reinterpret_cast<uint4*>(a.out + row * D + d0) = r;
+      uint32_t w4[PER / 2];
+#pragma unroll
+      for (int e = 0; e < PER / 2; ++e) w4[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      if constexpr (PER == 8)
+        *reinterpret_cast<uint4*>(a.out + row * D + d0) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      else
+        *reinterpret_cast<uint2*>(a.out + row * D + d0) = make_uint2(w4[0], w4[1]);
     } else {
       float* po = a.part_o + (row * a.S + s) * D + d0;
-      reinterpret_cast<float4*>(po)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      reinterpret_cast<float4*>(po)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+      for (int e = 0; e < PER; e += 4)
+        *reinterpret_cast<float4*>(po + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
       if (d0 == 0) {
         a.part_m[row * a.S + s] = M;
         a.part_l[row * a.S + s] = L;
@@ -249,61 +321,64 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialLaunch a) {
   }
 }
 
-// Log-sum-exp combine of S partials per output row. Splits with no valid key
-// (m = -inf) are skipped; the first non-empty split initialises the sums, so a
-// single non-empty split reproduces the one-split output bit for bit.
+// Log-sum-exp merge of the S split partials, one output row per wave. Split
+// weights 2^(m_s - M) are formed lane-parallel; empty splits (m = -inf) get
+// weight 0 and hold zeros. With one non-empty split the result equals the
+// one-split output bit for bit (its weight is exactly 1, every other term 0).
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(PartialLaunch a) {
+__global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
   constexpr int PER = D / 64;  // outputs per lane
-  const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* pm = a.part_m + row * a.S;
-  const float* pl = a.part_l + row * a.S;
-  const float* po = a.part_o + row * a.S * D;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.Hq) return;
+  const int S = a.S;
+  const float* pm = a.part_m + row * S;
+  const float* pl = a.part_l + row * S;
+  const float* po = a.part_o + row * S * D;
 
   float M = kNegInf;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, pm[s]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, pm[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  bool first = true;
   if (M != kNegInf) {
-    for (int s = 0; s < a.S; ++s) {
-      const float ms = pm[s];
-      if (ms == kNegInf) continue;
-      const float w = exp2_fast(ms - M);
-      if (first) {
-        L = pl[s] * w;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      const float ms = s < S ? pm[s] : kNegInf;
+      const float w = (ms == kNegInf) ? 0.f : exp2_fast(ms - M);
+      float lw = s < S ? pl[s] * w : 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = po[s * D + lane * PER + e] * w;
-        first = false;
-      } else {
-        L = L + pl[s] * w;
+      for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
+      L += lw;
+      const int n = (S - s0 < 64) ? S - s0 : 64;
+#pragma unroll 8
+      for (int i = 0; i < n; ++i) {
+        const float wi = __shfl(w, i);
+        const float* src = po + (int64_t)(s0 + i) * D + lane * PER;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = acc[e] + po[s * D + lane * PER + e] * w;
+        for (int e = 0; e < PER; ++e) acc[e] += wi * src[e];
       }
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  uint16_t* dst = a.out + row * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) dst[e] = (uint16_t)f32_to_bf16_rne(acc[e] * inv);
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(a.out + row * D + lane * 2) = pack_bf16(acc[0] * inv, acc[1] * inv);
+  } else {
+    a.out[row * D + lane] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+  }
 }
 
 template <int D, bool SPARSE>
 hipError_t launch_partial_d(const PartialLaunch& L, hipStream_t stream) {
   const int tiles = L.G / L.heads_per_wg;
   const int64_t grid = (int64_t)L.B * L.Hkv * tiles * L.S;
-  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(kThreads);
-  switch (L.heads_per_wg) {
-    case 1: hipLaunchKernelGGL((partial_kernel<D, 1, SPARSE>), g, blk, 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((partial_kernel<D, 2, SPARSE>), g, blk, 0, stream, L); break;
-    case 4: hipLaunchKernelGGL((partial_kernel<D, 4, SPARSE>), g, blk, 0, stream, L); break;
-    case 8: hipLaunchKernelGGL((partial_kernel<D, 8, SPARSE>), g, blk, 0, stream, L); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (grid <= 0 || grid > 0x7fffffff || L.heads_per_wg < 1 || L.heads_per_wg > 16)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attend_partial<D, SPARSE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     L);
   return hipGetLastError();
 }
 
@@ -319,11 +394,12 @@ hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream) {
   const int64_t rows = (int64_t)L.B * L.Hq;
-  if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int64_t blocks = (rows + 3) / 4;
+  if (rows <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (L.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)rows), dim3(64), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<128>, dim3((unsigned)blocks), dim3(256), 0, stream, L);
   else if (L.D == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)rows), dim3(64), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<64>, dim3((unsigned)blocks), dim3(256), 0, stream, L);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
