@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--force-splits", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device-to-device copy (a reference "
+                         "dispatch of known traffic for hardware-counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -220,6 +223,15 @@ def main():
     achieved = algo_bytes / kern_mean_s / 1e9
     log(f"{ms_per_step * 1e3:.1f} us/step, partial kernel mean {kern_mean_s * 1e6:.1f} us "
         f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f})")
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
 
     traffic = traffic_from_counters(args.workload)
     result = {

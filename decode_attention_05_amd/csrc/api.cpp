@@ -153,6 +153,10 @@ decode_attn_status validate_problem(const decode_attn_problem& p) {
   }
   if (p.num_cus < 0 || p.force_splits < 0 || p.force_chunk < 0)
     return fail(DA_ERR_INVALID_ARG, "num_cus, force_splits and force_chunk must be >= 0");
+  // The kernels address a KV row by a 32-bit byte offset inside one (batch, kv
+  // head) slab of capacity * head_dim bf16.
+  if ((double)p.capacity * p.head_dim * 2.0 >= 4294967296.0)
+    return fail(DA_ERR_UNSUPPORTED, "capacity: one kv head's rows must span less than 4 GiB");
   // Element counts must fit the 64-bit index arithmetic with ample margin.
   const double elems = (double)p.batch * p.num_kv_heads * (double)p.capacity * p.head_dim;
   if (elems > 9.0e15) return fail(DA_ERR_INVALID_ARG, "KV buffer too large");

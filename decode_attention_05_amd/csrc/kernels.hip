@@ -87,7 +87,7 @@ struct TileRegs {
 };
 
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
+__global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   using Gm = Geometry<D>;
   constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
 
@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
   __shared__ float mrg_l[kWaves][16];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar addressing
   const int g = lane >> 4;   // lane group: which 8 bf16 of a 32-wide k slice
   const int r16 = lane & 15; // A-operand row / C-operand column
 
@@ -136,37 +137,54 @@ __global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
 
   unsigned char* vt = lds + wave * Gm::VTILE;  // this wave's V tile
 
-  // Issue the loads of tile `tau` (tile index within the split) into R.
+  // Issue the loads of tile `tau` (tile index within the split) into R. Every
+  // load is unconditional, so the compiler can count them and wait only for the
+  // tile being processed: a slot without a valid key reads an allowed row (the
+  // last key of the split, or row 0 for a sparse pad), and its score and value
+  // are masked off before use. No row at or beyond k_len is ever read.
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kp);
+  const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vp);
   auto load_tile = [&](TileRegs<D>& R, int tau) {
     const int64_t kt = j0 + (int64_t)tau * kTileKeys;
-    int row_lane = -1;  // sparse: row of key (lane & 31) of the tile
+    const unsigned char* kb;
+    const unsigned char* vb;
+    int row_lane = 0;  // sparse: row of key (lane & 31) of the tile (0 for a pad)
+    int last = 0;      // dense: last valid slot of the tile
     if constexpr (SPARSE) {
       const int64_t t = kt + (lane & 31);
       const int32_t r = (tau < ntiles && t < j1) ? sel_row[t] : -1;
-      row_lane = (r >= 0 && (int64_t)r < a.k_len) ? (int)r : -1;
-      R.mask = (uint32_t)__ballot(row_lane >= 0);
+      const bool ok = r >= 0 && (int64_t)r < a.k_len;
+      row_lane = ok ? (int)r : 0;
+      R.mask = (uint32_t)__ballot(ok);
+      kb = kbytes;
+      vb = vbytes;
     } else {
       const int64_t n = (tau < ntiles) ? j1 - kt : 0;
       R.mask = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+      // A tile past the end re-reads the split's last key (cached, never used).
+      const int64_t base = n > 0 ? kt : j1 - 1;
+      last = n >= 32 ? 31 : (n > 0 ? (int)n - 1 : 0);
+      kb = kbytes + base * Gm::ROWB;
+      vb = vbytes + base * Gm::ROWB;
     }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int slot = 16 * sb + r16;
-      int64_t row;
-      if constexpr (SPARSE) row = __shfl(row_lane, slot);
-      else row = ((R.mask >> slot) & 1u) ? kt + slot : -1;
+      uint32_t row;
+      if constexpr (SPARSE) row = (uint32_t)__shfl(row_lane, slot);
+      else row = (uint32_t)(slot < last ? slot : last);
+      const uint32_t off = row * (uint32_t)Gm::ROWB + (uint32_t)g * 16u;  // uniform base + 32-bit offset
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        R.k[sb][c] = row >= 0 ? kp[row * RU4 + 4 * c + g] : make_uint4(0u, 0u, 0u, 0u);
+      for (int c = 0; c < NC; ++c) R.k[sb][c] = *reinterpret_cast<const uint4*>(kb + (off + 64u * c));
     }
 #pragma unroll
     for (int r = 0; r < VLD; ++r) {
       const int idx = r * 64 + lane;
       const int slot = idx / RU4, chunk = idx % RU4;
-      int64_t row;
-      if constexpr (SPARSE) row = __shfl(row_lane, slot);
-      else row = ((R.mask >> slot) & 1u) ? kt + slot : -1;
-      R.v[r] = row >= 0 ? vp[row * RU4 + chunk] : make_uint4(0u, 0u, 0u, 0u);
+      uint32_t row;
+      if constexpr (SPARSE) row = (uint32_t)__shfl(row_lane, slot);
+      else row = (uint32_t)(slot < last ? slot : last);
+      R.v[r] = *reinterpret_cast<const uint4*>(vb + (row * (uint32_t)Gm::ROWB + (uint32_t)chunk * 16u));
     }
   };
 
@@ -180,11 +198,22 @@ __global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
   auto process_tile = [&](const TileRegs<D>& R) {
     const uint32_t mask = R.mask;
     if (mask == 0u) return;  // nothing valid: the state is left untouched
-    // V tile -> LDS (swizzled), for the transposed reads below.
+    // V tile -> LDS (swizzled), for the transposed reads below. Rows of masked
+    // slots are zeroed so that a non-finite value there cannot reach the output.
+    if (mask == 0xffffffffu) {
 #pragma unroll
-    for (int r = 0; r < VLD; ++r) {
-      const int idx = r * 64 + lane;
-      *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) = R.v[r];
+      for (int r = 0; r < VLD; ++r) {
+        const int idx = r * 64 + lane;
+        *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) = R.v[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < VLD; ++r) {
+        const int idx = r * 64 + lane;
+        const bool ok = (mask >> (idx / RU4)) & 1u;
+        *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) =
+            ok ? R.v[r] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
     // S^T halves: keys 4g+i (first) and 16+4g+i (second) for head r16.
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -321,53 +350,65 @@ __global__ __launch_bounds__(kThreads) void attend_partial(PartialLaunch a) {
   }
 }
 
-// Log-sum-exp merge of the S split partials, one output row per wave. Split
-// weights 2^(m_s - M) are formed lane-parallel; empty splits (m = -inf) get
-// weight 0 and hold zeros. With one non-empty split the result equals the
-// one-split output bit for bit (its weight is exactly 1, every other term 0).
+// Log-sum-exp merge of the S split partials of one output row per workgroup.
+// M = max_s m_s; wave w accumulates the splits s = w, w + 4, ... with weights
+// 2^(m_s - M) (0 for an empty split, whose partial holds zeros); the four
+// waves are then summed in a fixed order. With one non-empty split its weight
+// is exactly 1 and every other term is an exact 0, so the result equals the
+// one-split output bit for bit.
 template <int D>
 __global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
   constexpr int PER = D / 64;  // outputs per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.B * a.Hq) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t row = blockIdx.x;
   const int S = a.S;
   const float* pm = a.part_m + row * S;
   const float* pl = a.part_l + row * S;
-  const float* po = a.part_o + row * S * D;
+  const float* po = a.part_o + row * S * D + lane * PER;
+  __shared__ float red_m[4];
+  __shared__ float red_l[4];
+  __shared__ float red_o[4][D];
 
   float M = kNegInf;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, pm[s]);
+  for (int j = tid; j < S; j += 256) M = fmaxf(M, pm[j]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
 
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   if (M != kNegInf) {
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const int s = s0 + lane;
-      const float ms = s < S ? pm[s] : kNegInf;
-      const float w = (ms == kNegInf) ? 0.f : exp2_fast(ms - M);
-      float lw = s < S ? pl[s] * w : 0.f;
+#pragma unroll 4
+    for (int j = wave; j < S; j += 4) {
+      const float mj = pm[j];
+      const float w = (mj == kNegInf) ? 0.f : exp2_fast(mj - M);
+      L += pl[j] * w;
+      const float* src = po + (int64_t)j * D;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
-      L += lw;
-      const int n = (S - s0 < 64) ? S - s0 : 64;
-#pragma unroll 8
-      for (int i = 0; i < n; ++i) {
-        const float wi = __shfl(w, i);
-        const float* src = po + (int64_t)(s0 + i) * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += wi * src[e];
-      }
+      for (int e = 0; e < PER; ++e) acc[e] += src[e] * w;
     }
   }
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(a.out + row * D + lane * 2) = pack_bf16(acc[0] * inv, acc[1] * inv);
-  } else {
-    a.out[row * D + lane] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+  if (lane == 0) red_l[wave] = L;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) red_o[wave][lane * PER + e] = acc[e];
+  __syncthreads();
+  if (wave == 0) {
+    L = ((red_l[0] + red_l[1]) + red_l[2]) + red_l[3];
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = lane * PER + e;
+      o[e] = (((red_o[0][d] + red_o[1][d]) + red_o[2][d]) + red_o[3][d]) * inv;
+    }
+    if constexpr (PER == 2)
+      *reinterpret_cast<uint32_t*>(a.out + row * D + lane * 2) = pack_bf16(o[0], o[1]);
+    else
+      a.out[row * D + lane] = (uint16_t)(pack_bf16(o[0], 0.f) & 0xffffu);
   }
 }
 
@@ -394,12 +435,11 @@ hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream) {
   const int64_t rows = (int64_t)L.B * L.Hq;
-  const int64_t blocks = (rows + 3) / 4;
-  if (rows <= 0 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (L.D == 128)
-    hipLaunchKernelGGL(combine_splits<128>, dim3((unsigned)blocks), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<128>, dim3((unsigned)rows), dim3(256), 0, stream, L);
   else if (L.D == 64)
-    hipLaunchKernelGGL(combine_splits<64>, dim3((unsigned)blocks), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<64>, dim3((unsigned)rows), dim3(256), 0, stream, L);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
