@@ -247,7 +247,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": dict(workload=desc, splits=splits, kv_sets=sets,
                        algorithmic_bytes_per_step=algo_bytes, **cfg),
