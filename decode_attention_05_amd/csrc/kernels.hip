@@ -48,6 +48,16 @@ constexpr int kTileKeys = 32;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load with the non-temporal hint (K and V are read exactly
+// once per call): measured on MI355X at ~7 TB/s for a plain read stream, against
+// ~6 TB/s with the default cache policy.
+__device__ __forceinline__ uint4 load_stream(const unsigned char* base, uint32_t off) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
       else row = (uint32_t)(slot < last ? slot : last);
       const uint32_t off = row * (uint32_t)Gm::ROWB + (uint32_t)g * 16u;  // uniform base + 32-bit offset
 #pragma unroll
-      for (int c = 0; c < NC; ++c) R.k[sb][c] = *reinterpret_cast<const uint4*>(kb + (off + 64u * c));
+      for (int c = 0; c < NC; ++c) R.k[sb][c] = load_stream(kb, off + 64u * c);
     }
 #pragma unroll
     for (int r = 0; r < VLD; ++r) {
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
       uint32_t row;
       if constexpr (SPARSE) row = (uint32_t)__shfl(row_lane, slot);
       else row = (uint32_t)(slot < last ? slot : last);
-      R.v[r] = *reinterpret_cast<const uint4*>(vb + (row * (uint32_t)Gm::ROWB + (uint32_t)chunk * 16u));
+      R.v[r] = load_stream(vb, row * (uint32_t)Gm::ROWB + (uint32_t)chunk * 16u);
     }
   };
 
