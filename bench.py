@@ -137,7 +137,9 @@ def main():
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--force-splits", type=int, default=0)
+    ap.add_argument("--force-splits", type=int, default=0, help="dense split count (tuning)")
+    ap.add_argument("--force-chunk", type=int, default=0,
+                    help="keys (dense) or selection entries (sparse) per split (tuning)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -179,11 +181,11 @@ def main():
     out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
     if sparse:
         plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.rows, topk_max=case.topk,
-                                   kv_batch=case.kv_batch)
+                                   kv_batch=case.kv_batch, force_chunk=args.force_chunk)
         splits = -(-case.topk // plan.chunk)
     else:
         plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.capacity, case.k_len,
-                                   force_splits=args.force_splits)
+                                   force_splits=args.force_splits, force_chunk=args.force_chunk)
         splits = plan.num_splits_max
     ws = da.workspace_for(plan)
 

@@ -107,17 +107,22 @@ def test_invalid_problems(da, kw):
 
 
 def test_dense_plans_for_the_workloads(da):
-    # split counts with 256 compute units: enough workgroups to fill the chip,
-    # never fewer than 256 keys per split
+    # With 256 compute units: split only when there are fewer (batch, kv head)
+    # units than CUs, fill 2 resident workgroups per CU once, keep >= 1024 keys
+    # per split.
     tiny = da.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256)
-    assert tiny.num_splits_max == 2 and tiny.workspace_bytes == 1 * 8 * 2 * 66 * 4
+    assert tiny.num_splits_max == 1 and tiny.workspace_bytes == 0
     gqa = da.decode_attn_plan(8, 32, 8, 128, 8192, 4096, num_cus=256)
-    assert gqa.num_splits_max == 16 and gqa.chunk == 256
+    assert gqa.num_splits_max == 4 and gqa.chunk == 1024
+    assert gqa.workspace_bytes == 8 * 32 * 4 * 130 * 4
     long = da.decode_attn_plan(4, 64, 8, 128, 131072, 131072, num_cus=256)
-    assert long.num_splits_max == 32 and long.chunk == 4096
-    assert long.workspace_bytes == 4 * 64 * 32 * 130 * 4
+    assert long.num_splits_max == 16 and long.chunk == 8192
+    assert long.workspace_bytes == 4 * 64 * 16 * 130 * 4
     batch = da.decode_attn_plan(128, 32, 8, 128, 2048, 1537, num_cus=256)
     assert batch.num_splits_max == 1 and batch.workspace_bytes == 0
+    # query heads beyond 16 per kv head are served by several head tiles
+    wide = da.decode_attn_plan(4, 64, 1, 128, 8192, 8192, num_cus=256)
+    assert wide.group == 64 and wide.num_splits_max == 8  # 16 units -> 32 splits, capped at 8192/1024
 
 
 def test_sparse_plan_chunk_is_independent_of_call(da):
