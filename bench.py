@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,10 +50,15 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    stored counter readings stay valid across comment-only edits."""
     h = hashlib.sha256()
     for fn in ("kernels.hip", "device_common.h", "launch.h"):
-        with open(os.path.join(ROOT, "decode_attention_05_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "decode_attention_05_amd", "csrc", fn)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,8 +4,8 @@
 // (fuel-dispatch page "DecodeFlashSpec": q [B, Hq, 1, D] against the capacity
 // buffers [B, Hkv, capacity, D] over the live prefix [0, k_len), grouped-query
 // heads), and its index-selected form (metrale page "AttnV41",
-// decode_fixed_topk: rows named by a -1-padded selection, a pad adding exactly
-// zero).
+// decode_fixed_topk: rows named by a -1-padded selection; pads contribute
+// nothing).
 //
 // Decomposition (split-K over keys): one workgroup owns a (batch, kv head,
 // head tile, split); each of its four waves streams every fourth 32-key tile

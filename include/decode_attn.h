@@ -17,8 +17,8 @@
  *
  * The sparse variant follows the metrale page "AttnV41" (decode_fixed_topk,
  * decode_prep, decode_body): each token attends the KV rows listed in its
- * selection, padded with -1 to a fixed launch width topk; a pad adds exactly
- * zero to the softmax denominator and nothing to the output, so padding the
+ * selection, padded with -1 to a fixed launch width topk; a pad contributes
+ * to neither the softmax sum nor the weighted sum of values, so padding the
  * same valid entries to any width gives bit-identical output.
  *
  * Conventions (every call):

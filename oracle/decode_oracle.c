@@ -15,7 +15,7 @@
  *     there as the oracle (field decomposed_out): this file plays that role.
  *   - metrale page "AttnV41", decode_fixed_topk and decode_prep: in the sparse
  *     variant each token attends the rows named by its padded selection; a -1
- *     entry adds exactly zero to the denominator and nothing to the output.
+ *     pad contributes to neither the softmax sum nor the weighted sum of values.
  *
  * Readings where the pages are silent (each one is listed in the design notes):
  *   - query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups);
