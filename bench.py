@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing of the plan-once call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--force-splits", type=int, default=0, help="dense split count (tuning)")
     ap.add_argument("--force-chunk", type=int, default=0,
@@ -232,6 +234,39 @@ def main():
     log(f"{ms_per_step * 1e3:.1f} us/step, partial kernel mean {kern_mean_s * 1e6:.1f} us "
         f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f})")
 
+    # Plan-once decode: the same step captured once in a HIP graph (dense: the call
+    # that reads k_len from device memory) and replayed; one replay runs every K/V
+    # set once.
+    graph_us = None
+    if not args.no_graph:
+        klen_dev = torch.full((1,), 0 if sparse else case.k_len, dtype=torch.int32, device="cuda")
+
+        def gstep(i):
+            kk, vv = dks[i % sets], dvs[i % sets]
+            if sparse:
+                da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows,
+                                      ws)
+            else:
+                da.decode_attn_dense_devlen(plan, dq, kk, vv, out, case.scale, klen_dev, ws)
+
+        gstep(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(sets):
+                gstep(i)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // sets)
+        g0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - g0) * 1e6 / (reps * sets)
+        log(f"graph replay: {graph_us:.1f} us/step")
+        del graph
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -273,6 +308,7 @@ def main():
             "bytes_per_launch": algo_bytes,
         },
         "cpu_baseline": None,
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

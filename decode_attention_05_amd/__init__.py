@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
-    "decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
+    "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_sparse",
     "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
     "workspace_for",
     "EXPORTED_SYMBOLS",
@@ -30,7 +30,8 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
-EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
+EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
+                    "decode_attn_sparse",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
 
@@ -87,6 +88,9 @@ def library():
         lib.decode_attn_dense.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
                                           ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_dense.restype = ctypes.c_int
+        lib.decode_attn_dense_devlen.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
+                                                 P, P, ctypes.c_size_t, P]
+        lib.decode_attn_dense_devlen.restype = ctypes.c_int
         lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
                                            ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_sparse.restype = ctypes.c_int
@@ -193,6 +197,23 @@ def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense(ctypes.byref(plan), *args, float(softmax_scale), int(k_len),
                                        ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_len_dev,
+                             workspace=None, stream=None):
+    """Dense decode attention whose live length is the int32 in ``k_len_dev`` (a
+    one-element device tensor), read by the kernel: capturable once, replayable."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    bf = torch.bfloat16
+    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    klen = _tensor_ptr(k_len_dev, "k_len_dev", (1,), torch.int32)
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_dense_devlen(ctypes.byref(plan), *args, float(softmax_scale),
+                                              klen, ws, wsb, _stream_ptr(stream)))
     return out
 
 

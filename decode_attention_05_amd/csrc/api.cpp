@@ -331,6 +331,30 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
   return run(L, stream);
 }
 
+decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, const int32_t* k_len_dev,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  decode_attn_status s =
+      check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
+  if (s != DA_OK) return s;
+  if (!k_len_dev) return fail(DA_ERR_INVALID_ARG, "k_len_dev must be non-NULL");
+  if (((uintptr_t)k_len_dev & 3u) != 0)
+    return fail(DA_ERR_INVALID_ARG, "k_len_dev must be 4-byte aligned");
+  // The launch is sized once for max_k_len; the kernel spreads whatever length
+  // the device holds over the same splits.
+  const int S = plan->num_splits_max;
+  da::PartialLaunch L =
+      base_launch(*plan, q, k, v, out, softmax_scale, plan->prob.max_k_len, workspace, S);
+  L.k_len_dev = k_len_dev;
+  L.chunk = plan->chunk;
+  L.sparse = false;
+  if (log_enabled())
+    std::fprintf(stderr, "[decode_attn] dense (device k_len) splits=%d\n", S);
+  return run(L, stream);
+}
+
 decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void* q, const void* k,
                                       const void* v, const int32_t* sel, int32_t topk, void* out,
                                       float softmax_scale, int64_t k_len, void* workspace,

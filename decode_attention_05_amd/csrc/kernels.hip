@@ -138,10 +138,25 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   const uint4* __restrict__ kp = reinterpret_cast<const uint4*>(a.k + kv_base);
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(a.v + kv_base);
 
+  // Live length and split size. With a device-resident length (plan-once
+  // decode) the S splits share [0, k_len) evenly for whatever k_len the device
+  // holds; a value outside [0, max_k_len] is clamped, and k_len = 0 yields zeros.
+  int64_t k_len = a.k_len;
+  int64_t chunk = a.chunk;
+  if constexpr (!SPARSE) {
+    if (a.k_len_dev) {
+      const int64_t raw = __builtin_amdgcn_readfirstlane(*a.k_len_dev);
+      k_len = raw < 0 ? 0 : (raw > a.k_len ? a.k_len : raw);
+      chunk = (k_len + a.S - 1) / a.S;
+      chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+      if (chunk == 0) chunk = kTileKeys;
+    }
+  }
+
   // This split: keys (dense) or selection entries (sparse) [j0, j1).
-  const int64_t j0 = (int64_t)s * a.chunk;
-  const int64_t j_end = SPARSE ? (int64_t)a.topk : a.k_len;
-  const int64_t j1 = (j0 + a.chunk < j_end) ? j0 + a.chunk : j_end;
+  const int64_t j0 = (int64_t)s * chunk;
+  const int64_t j_end = SPARSE ? (int64_t)a.topk : k_len;
+  const int64_t j1 = (j0 + chunk < j_end) ? j0 + chunk : j_end;
   const int ntiles = (j1 > j0) ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
   const int32_t* sel_row = SPARSE ? a.sel + (int64_t)b * a.topk : nullptr;
 

@@ -12,6 +12,8 @@ struct PartialLaunch {
   const uint16_t* k;   // [kv_batch, Hkv, capacity, D] bf16
   const uint16_t* v;
   const int32_t* sel;  // sparse only: [B, topk]
+  const int32_t* k_len_dev;  // dense, optional: k_len read on the device (k_len then
+                             // holds its upper bound, the plan's max_k_len)
   uint16_t* out;       // [B, Hq, 1, D] bf16: written directly when S == 1
   float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1)
   float* part_m;       // [B*Hq, S] running max, base 2 (S > 1)

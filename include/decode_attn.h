@@ -124,6 +124,26 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * Dense decode attention with the live length read on the device (plan-once
+ * decode: DecodeFlashSpec's k_len as a symbol bound to the live length each
+ * token, fuel-dispatch page "DecodeFlashSpec", field k_len). Same arguments
+ * as decode_attn_dense except:
+ *   k_len_dev  device pointer to one int32, read by the kernel when it runs. The
+ *          launch is sized once for plan->prob.max_k_len, so the call can be
+ *          captured in a HIP graph and replayed while the caller rewrites the
+ *          value between replays. The value is caller-owned and not validated on
+ *          the host: a value above max_k_len is clamped to max_k_len, and a value
+ *          <= 0 produces zero output. Rows at or beyond the clamped length are
+ *          never read.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_WORKSPACE or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, const int32_t* k_len_dev,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/*
  * Index-selected sparse decode attention.
  *   q    [B, Hq, 1, D] bf16           k, v [kv_batch, Hkv, capacity, D] bf16
  *   sel  [B, topk] int32 (device): token b attends rows sel[b, t] of its KV set

@@ -33,8 +33,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(da):
     names = declared_functions()
-    assert {"decode_attn_plan", "decode_attn_dense", "decode_attn_sparse",
-            "decode_attn_status_str", "decode_attn_last_error"} <= names
+    assert {"decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
+            "decode_attn_sparse", "decode_attn_status_str", "decode_attn_last_error"} <= names
     lib = ctypes.CDLL(da.library_path)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -169,6 +169,13 @@ def test_compute_calls_fail_closed_before_any_launch(da):
     assert scall(fake, 64, 0) == 1
     assert scall(None, 64, 1000) == 1
     assert scall(ctypes.c_void_p(0x10002), 64, 1000) == 1
+    # device-resident length: NULL or misaligned pointer
+    dl = lambda p: lib.decode_attn_dense_devlen(ctypes.byref(P), fake, fake, fake, fake, 0.1, p, ws,  # noqa: E731
+                                                P.workspace_bytes, None)
+    assert dl(None) == 1
+    assert dl(ctypes.c_void_p(0x10002)) == 1
+    assert lib.decode_attn_dense_devlen(ctypes.byref(S), fake, fake, fake, fake, 0.1, fake, ws,
+                                        S.workspace_bytes, None) == 1
     # the dense plan handed to the sparse call
     assert lib.decode_attn_sparse(ctypes.byref(P), fake, fake, fake, fake, 8, fake, 0.1, 10, ws,
                                   P.workspace_bytes, None) == 1
