@@ -10,9 +10,11 @@ in the design notes):
   max(0, pos - window + 1) .. pos, oldest first; position p lives in KV row
   ``win_base + p % window``; a negative pos gives an empty window;
 * the index selection is the ``k`` candidates 0 .. n_idx-1 with the largest
-  scores, in descending score order, ties broken by the lower candidate index,
-  where k = min(k_idx, n_idx, topk - window entries) (never negative); scores
-  are ordered by the IEEE 754 totalOrder predicate (so -0 sorts below +0);
+  scores, ties broken by the lower candidate index, where k = min(k_idx, n_idx,
+  topk - window entries) (never negative); scores are ordered by the IEEE 754
+  totalOrder predicate (so -0 sorts below +0). The page does not fix the order
+  of the rows inside the index selection (it only changes rounding in the
+  attention): they are listed in ascending row order;
 * every remaining entry is -1.
 
 Plain Python loops and ``sorted``: slow, obviously correct. Pinned by
@@ -49,6 +51,6 @@ def build_selection(scores: np.ndarray, pos, n_idx: int, k_idx: int, window: int
         k = max(0, min(k_idx, n_idx, topk - n_win))
         keys = [total_order_key(scores[b, i]) for i in range(n_idx)]
         ranked = sorted(range(n_idx), key=lambda i: (-keys[i], i))
-        row.extend(ranked[:k])
+        row.extend(sorted(ranked[:k]))
         out[b, :len(row)] = row
     return out

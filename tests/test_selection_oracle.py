@@ -22,22 +22,24 @@ def test_window_only_closed_form():
                             [-1, -1, -1, -1, -1]]
 
 
-def test_index_part_is_top_k_by_score_then_index():
+def test_index_part_is_top_k_by_score_listed_by_row():
     s = np.array([[0.5, 3.0, -1.0, 3.0, 2.0, 7.0]], np.float32)
     sel = build_selection(s, [0], 6, 4, 0, 0, 6)
-    assert sel.tolist() == [[5, 1, 3, 4, -1, -1]]   # 7, then the tie 3,3 by index, then 2
+    assert sel.tolist() == [[1, 3, 4, 5, -1, -1]]   # rows of 7, 3, 3, 2, ascending
+    # a tie at the cut goes to the lower index: of the two 3.0s only row 1 fits
+    assert build_selection(s, [0], 6, 2, 0, 0, 6).tolist() == [[1, 5, -1, -1, -1, -1]]
 
 
 def test_width_limits_the_index_part():
     s = np.arange(10, dtype=np.float32)[None, :]
     sel = build_selection(s, [5], 10, 8, 3, 50, 6)
     # 3 window rows (positions 3, 4, 5 -> rows 50 + p % 3), then 6 - 3 = 3 best indices
-    assert sel.tolist() == [[50, 51, 52, 9, 8, 7]]
+    assert sel.tolist() == [[50, 51, 52, 7, 8, 9]]
 
 
 def test_k_larger_than_candidates():
     s = np.array([[1.0, 2.0]], np.float32)
-    assert build_selection(s, [0], 2, 5, 0, 0, 4).tolist() == [[1, 0, -1, -1]]
+    assert build_selection(s, [0], 2, 5, 0, 0, 4).tolist() == [[0, 1, -1, -1]]
 
 
 @pytest.mark.parametrize("seed", [1, 2])
@@ -51,7 +53,7 @@ def test_matches_numpy_lexsort(seed):
     for b in range(B):
         order = np.lexsort((np.arange(n), -s[b].astype(np.float64)))[:k]
         n_win = min(pos[b] + 1, 64)
-        assert sel[b, n_win:n_win + k].tolist() == order.tolist()
+        assert sel[b, n_win:n_win + k].tolist() == sorted(order.tolist())
         assert (sel[b, n_win + k:] == -1).all()
         win = [n + p % 64 for p in range(pos[b] - n_win + 1, pos[b] + 1)]
         assert sel[b, :n_win].tolist() == win
