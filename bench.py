@@ -134,13 +134,106 @@ def cpu_baseline(args, case, host, algo_bytes, W):
     }
 
 
+def bench_selection(args, torch, np, da, W, H):
+    """The on-device selection builder on the sparse workload's shapes ("select"),
+    or builder + sparse attention as one step ("sparse_built"): 4 tokens, 65408
+    scored index candidates, 1920 chosen, a 128-slot window ring, width 2048."""
+    case = W.SPARSE_CASES["sparse"]
+    n_idx = case.rows - case.window
+    k_idx = case.topk - case.window
+    rng = np.random.Generator(np.random.PCG64(90))
+    scores = rng.standard_normal((case.B, n_idx), dtype=np.float32)
+    pos = np.array([70000 + 13 * b for b in range(case.B)], np.int32)
+    dsc = torch.from_numpy(scores).cuda()
+    dpos = torch.from_numpy(pos).cuda()
+    dsel = torch.empty((case.B, case.topk), dtype=torch.int32, device="cuda")
+    sel_bytes = scores.nbytes + pos.nbytes + case.B * case.topk * 4
+    built = args.workload == "sparse_built"
+    if built:
+        log("generating sparse inputs (seed 5)")
+        q, k, v, _ = W.sparse_inputs(case)
+        dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+        out = torch.empty((case.B, case.Hq, 1, case.D), dtype=torch.bfloat16, device="cuda")
+        plan = da.decode_attn_plan(case.B, case.Hq, case.Hkv, case.D, case.rows,
+                                   topk_max=case.topk, kv_batch=1)
+        ws = da.workspace_for(plan)
+        algo_bytes = sel_bytes + case.algorithmic_bytes() - case.B * case.topk * 4
+    else:
+        algo_bytes = sel_bytes
+
+    def step():
+        da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
+        if built:
+            da.decode_attn_sparse(plan, dq, dk, dv, dsel, case.topk, out, case.scale, case.rows, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev_b[i].record(stream)
+        da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
+        ev_a[i].record(stream)
+        if built:
+            da.decode_attn_sparse(plan, dq, dk, dv, dsel, case.topk, out, case.scale, case.rows, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = np.array([ev_b[i].elapsed_time(ev_a[i]) for i in range(args.steps)])
+    us = (t1 - t0) * 1e6 / args.steps
+    kern_us = float(kern_ms.mean()) * 1e3
+    log(f"{us:.1f} us/step, selection kernel mean {kern_us:.1f} us")
+    graph_us = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
+        log(f"graph replay: {graph_us:.1f} us/step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.selection import build_selection
+        t = time.perf_counter()
+        build_selection(scores[:1], pos[:1], n_idx, k_idx, case.window, n_idx, case.topk)
+        per_token = time.perf_counter() - t
+        cpu = {"value": round(sel_bytes / (per_token * case.B) / 1e9, 6), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"selection of 1 of {case.B} tokens, {per_token:.2f} s, scaled to {case.B}"}
+    value = algo_bytes / (us * 1e-6) / 1e9
+    desc = ("selection builder" + (" + sparse attention" if built else "") +
+            f": B={case.B} candidates={n_idx} k={k_idx} window={case.window} topk={case.topk}")
+    print(json.dumps({
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6),
+        "us_per_step": round(us, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if not built else "bf16", "data": "synthetic",
+        "config": {"workload": desc, "algorithmic_bytes_per_step": algo_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(sel_bytes / (kern_us * 1e-6) / 1e9, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(sel_bytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+                     "traffic": None, "kernel": "selection builder",
+                     "kernel_us_mean": round(kern_us, 3), "bytes_per_launch": sel_bytes},
+        "cpu_baseline": cpu,
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
-                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed"])
+                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "select",
+                             "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing of the plan-once call")
@@ -173,6 +266,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     da.library()
+
+    if args.workload in ("select", "sparse_built"):
+        return bench_selection(args, torch, np, da, W, H)
 
     case, host, kv_alloc, desc, cfg, algo_bytes = build_inputs(args, torch, W, H)
     sparse = host["sel"] is not None

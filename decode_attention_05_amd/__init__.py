@@ -20,6 +20,7 @@ import os
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_sparse",
+    "decode_attn_build_selection", "SelectProblem",
     "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
     "workspace_for",
     "EXPORTED_SYMBOLS",
@@ -31,7 +32,7 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
 EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
-                    "decode_attn_sparse",
+                    "decode_attn_sparse", "decode_attn_build_selection",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
 
@@ -64,6 +65,15 @@ class Plan(ctypes.Structure):
         return self.kind == 1
 
 
+class SelectProblem(ctypes.Structure):
+    """Mirror of ``decode_attn_select_problem``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_idx", ctypes.c_int32), ("score_stride", ctypes.c_int64),
+        ("k_idx", ctypes.c_int32), ("window", ctypes.c_int32), ("win_base", ctypes.c_int64),
+        ("topk", ctypes.c_int32),
+    ]
+
+
 class DecodeAttnError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -94,6 +104,8 @@ def library():
         lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
                                            ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_sparse.restype = ctypes.c_int
+        lib.decode_attn_build_selection.argtypes = [ctypes.POINTER(SelectProblem), P, P, P, P]
+        lib.decode_attn_build_selection.restype = ctypes.c_int
         lib.decode_attn_set_timing_events.argtypes = [P, P]
         lib.decode_attn_set_timing_events.restype = ctypes.c_int
         lib.decode_attn_status_str.argtypes = [ctypes.c_int]
@@ -234,3 +246,20 @@ def decode_attn_sparse(plan: Plan, q, k, v, sel, topk: int, out, softmax_scale: 
                                         float(softmax_scale), int(cap if k_len is None else k_len),
                                         ws, wsb, _stream_ptr(stream)))
     return out
+
+
+def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window: int,
+                                win_base: int, stream=None):
+    """Fill ``sel`` [B, topk] int32 on the device: window ring rows, then the k_idx
+    best-scoring candidates of ``scores`` [B, >= n_idx] fp32, then -1 (``pos`` [B] int32)."""
+    import torch
+    B, topk = sel.shape
+    stride = scores.shape[1]
+    prob = SelectProblem(B, int(n_idx), int(stride), int(k_idx), int(window), int(win_base),
+                         int(topk))
+    sp = _tensor_ptr(scores, "scores", (B, stride), torch.float32)
+    pp = _tensor_ptr(pos, "pos", (B,), torch.int32)
+    selp = _tensor_ptr(sel, "sel", (B, topk), torch.int32)
+    _check(library().decode_attn_build_selection(ctypes.byref(prob), sp, pp, selp,
+                                                 _stream_ptr(stream)))
+    return sel

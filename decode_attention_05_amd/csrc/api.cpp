@@ -21,6 +21,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "select.h"
 
 namespace {
 
@@ -379,6 +380,49 @@ decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void
   if (log_enabled())
     std::fprintf(stderr, "[decode_attn] sparse topk=%d splits=%d chunk=%d\n", topk, S, plan->chunk);
   return run(L, stream);
+}
+
+decode_attn_status decode_attn_build_selection(const decode_attn_select_problem* p,
+                                               const float* scores, const int32_t* pos,
+                                               int32_t* sel, void* stream) {
+  if (!p) return fail(DA_ERR_INVALID_ARG, "problem pointer must be non-NULL");
+  if (p->batch < 1 || p->topk < 1 || p->n_idx < 0 || p->window < 0 || p->k_idx < 0)
+    return fail(DA_ERR_INVALID_ARG, "batch and topk must be >= 1; n_idx, window, k_idx >= 0");
+  if (p->k_idx > da::kSelectMaxK)
+    return fail(DA_ERR_INVALID_ARG, "k_idx must be <= %d, got %d", da::kSelectMaxK, p->k_idx);
+  if (p->n_idx > da::kSelectMaxCandidates)
+    return fail(DA_ERR_UNSUPPORTED, "n_idx: at most %d index candidates per token, got %d",
+                da::kSelectMaxCandidates, p->n_idx);
+  if (p->score_stride < p->n_idx || p->score_stride < 1)
+    return fail(DA_ERR_INVALID_ARG, "score_stride must be >= max(n_idx, 1)");
+  if (p->win_base < 0 || p->win_base + p->window > 0x7fffffffLL)
+    return fail(DA_ERR_INVALID_ARG, "window rows must lie in [0, 2^31)");
+  if (p->n_idx > 0x7fffffff - 1 || (int64_t)p->batch * p->topk > 0x7fffffffLL)
+    return fail(DA_ERR_INVALID_ARG, "selection too large");
+  if (!pos || !sel) return fail(DA_ERR_INVALID_ARG, "pos and sel must be non-NULL");
+  if (((uintptr_t)pos & 3u) || ((uintptr_t)sel & 3u))
+    return fail(DA_ERR_INVALID_ARG, "pos and sel must be 4-byte aligned");
+  if (p->k_idx > 0 && p->n_idx > 0) {
+    if (!scores) return fail(DA_ERR_INVALID_ARG, "scores must be non-NULL when k_idx > 0");
+    if (((uintptr_t)scores & 15u) || (p->score_stride & 3))
+      return fail(DA_ERR_INVALID_ARG,
+                  "scores must be 16-byte aligned with a row stride that is a multiple of 4");
+  }
+  da::SelectLaunch L{};
+  L.scores = scores;
+  L.score_stride = p->score_stride;
+  L.pos = pos;
+  L.sel = sel;
+  L.B = p->batch;
+  L.n_idx = p->n_idx;
+  L.k_idx = p->k_idx;
+  L.window = p->window;
+  L.topk = p->topk;
+  L.win_base = p->win_base;
+  const hipError_t e = da::launch_select(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after) {

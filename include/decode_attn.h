@@ -166,6 +166,40 @@ decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void
                                       void* stream);
 
 /*
+ * The selection a sparse call reads, built on the device (metrale page
+ * "AttnV41": decode_prep / decode_prep_role fill the selection buffer with the
+ * window slots, then the shared index selection, then -1 up to the fixed width
+ * of decode_fixed_topk; decode_body writes the window as a ring at
+ * pos % window). Host struct.
+ */
+typedef struct {
+  int32_t batch;        /* B >= 1 tokens                                              */
+  int32_t n_idx;        /* index candidates 0 .. n_idx-1 per token, 0 .. 131072       */
+  int64_t score_stride; /* floats between rows of scores: >= n_idx, a multiple of 4    */
+  int32_t k_idx;        /* index entries to select per token, 0 .. 4096 (0: window only) */
+  int32_t window;       /* window ring slots W (>= 0)                                 */
+  int64_t win_base;     /* KV row of ring slot 0; the ring is rows win_base .. +W-1    */
+  int32_t topk;         /* launch width of the selection (>= 1)                       */
+} decode_attn_select_problem;
+
+/*
+ * Build sel [B, topk] int32 on `stream` from device scores [B, score_stride]
+ * fp32 and device positions pos [B] int32 (0-based position of each token).
+ * Row b holds: the window rows of positions max(0, pos-W+1) .. pos oldest first
+ * (position p in row win_base + p % W; none when pos < 0); then the
+ * min(k_idx, n_idx, topk - window entries) candidates with the largest scores
+ * (ties to the lower index; scores ordered by IEEE 754 totalOrder), listed in
+ * ascending row order; then -1. Device values are caller-owned (no host
+ * validation). scores must be 16-byte aligned; pos and sel 4-byte aligned.
+ * One kernel, no allocation, capturable.
+ * Returns DA_OK, DA_ERR_INVALID_ARG (shapes, NULL or misaligned pointers,
+ * k_idx > 4096), DA_ERR_UNSUPPORTED (n_idx > 131072) or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_build_selection(const decode_attn_select_problem* p,
+                                               const float* scores, const int32_t* pos,
+                                               int32_t* sel, void* stream);
+
+/*
  * Diagnostics: time the split-K partial kernel (the kernel that streams K and V)
  * with caller-created HIP events. After this call, every compute call made on
  * the calling thread records `ev_before` on its stream immediately before

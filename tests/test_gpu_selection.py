@@ -1,0 +1,121 @@
+"""The on-device selection builder against the selection oracle (exact, integers),
+and the built selection feeding the sparse attention, eager and in a HIP graph."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle.selection import build_selection
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def da():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.ensure_built()
+    import decode_attention_05_amd as m
+    m.library()
+    return m
+
+
+def run_builder(da, scores, pos, n_idx, k_idx, window, win_base, topk):
+    import torch
+    # rows padded to a multiple of 4 floats (the builder reads 16-byte vectors)
+    B, n = scores.shape
+    stride = max(4, (n + 3) // 4 * 4)
+    padded = np.full((B, stride), np.nan, np.float32)
+    padded[:, :n] = scores
+    sc = torch.from_numpy(padded).cuda()
+    ps = torch.from_numpy(np.asarray(pos, np.int32)).cuda()
+    sel = torch.full((scores.shape[0], topk), 12345, dtype=torch.int32, device="cuda")
+    da.decode_attn_build_selection(sc, ps, sel, n_idx, k_idx, window, win_base)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()
+
+
+def scores_for(seed, B, n, kind="normal"):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = rng.standard_normal((B, n), dtype=np.float32)
+    if kind == "ties":
+        s = np.round(s * 2) / 2          # a handful of distinct values
+    elif kind == "special":
+        s[:, ::97] = np.inf
+        s[:, 1::89] = -np.inf
+        s[:, 2::83] = 0.0
+        s[:, 3::79] = -0.0
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+def test_sparse_workload_shapes(da, kind):
+    # 4 tokens, 65408 index candidates, 1920 chosen, a 128-slot window ring at the
+    # top of 65536 rows, launch width 2048.
+    B, rows, W_, topk, k = 4, 65536, 128, 2048, 1920
+    n_idx = rows - W_
+    s = scores_for(80, B, n_idx, kind)
+    pos = [200000, 127, 0, 50]
+    H.log(f"selection builder kind={kind}")
+    got = run_builder(da, s, pos, n_idx, k, W_, n_idx, topk)
+    want = build_selection(s, pos, n_idx, k, W_, n_idx, topk)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("B,n_idx,k_idx,window,topk,pos", [
+    (2, 5, 10, 0, 8, [0, 3]),            # k larger than the candidates
+    (3, 1000, 300, 64, 100, [10, 500, 63]),  # the width cuts the index part
+    (2, 3000, 0, 16, 32, [5, 40]),       # window only
+    (2, 9000, 4096, 8, 4200, [3, 7]),    # the largest k
+    (2, 100, 20, 4, 30, [-1, 2]),        # negative position: no window rows
+    (1, 0, 5, 4, 6, [9]),                # no candidates
+    (5, 1, 1, 1, 1, [0, 1, 2, 3, 4]),    # width 1: only the newest window row
+])
+def test_edge_shapes(da, B, n_idx, k_idx, window, topk, pos):
+    s = scores_for(81 + n_idx, B, max(n_idx, 1))
+    got = run_builder(da, s, pos, n_idx, k_idx, window, 7000, topk)
+    assert np.array_equal(got, build_selection(s, pos, n_idx, k_idx, window, 7000, topk))
+
+
+def test_built_selection_feeds_sparse_attention(da):
+    import torch
+    case = W.SPARSE_CASES["sparse"]
+    _, (q, k, v, _) = H.sparse_case_inputs("sparse")
+    n_idx = case.rows - case.window
+    s = scores_for(82, case.B, n_idx)
+    pos = [70000, 90, 131, 5000]
+    sel_ref = build_selection(s, pos, n_idx, 1920, case.window, n_idx, case.topk)
+    plan = da.decode_attn_plan(case.B, case.Hq, case.Hkv, case.D, case.rows, topk_max=case.topk,
+                               kv_batch=1)
+    dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+    sc = torch.from_numpy(s).cuda()
+    ps = torch.from_numpy(np.asarray(pos, np.int32)).cuda()
+    sel = torch.empty((case.B, case.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((case.B, case.Hq, 1, case.D), dtype=torch.bfloat16, device="cuda")
+    ws = da.workspace_for(plan)
+    da.decode_attn_build_selection(sc, ps, sel, n_idx, 1920, case.window, n_idx)
+    da.decode_attn_sparse(plan, dq, dk, dv, sel, case.topk, out, case.scale, case.rows, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), sel_ref)
+    H.check_tolerance(H.from_dev(out), oracle.sparse(q, k, v, sel_ref, case.scale), "built")
+
+    # the same two calls captured once; scores and positions change between replays
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        da.decode_attn_build_selection(sc, ps, sel, n_idx, 1920, case.window, n_idx)
+        da.decode_attn_sparse(plan, dq, dk, dv, sel, case.topk, out, case.scale, case.rows, ws)
+    for it in range(3):
+        s2 = scores_for(83 + it, case.B, n_idx)
+        pos2 = [1000 * it + b for b in range(case.B)]
+        sc.copy_(torch.from_numpy(s2).cuda())
+        ps.copy_(torch.from_numpy(np.asarray(pos2, np.int32)).cuda())
+        H.log(f"selection+attention graph replay {it}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref_sel = build_selection(s2, pos2, n_idx, 1920, case.window, n_idx, case.topk)
+        assert np.array_equal(sel.cpu().numpy(), ref_sel)
+        H.check_tolerance(H.from_dev(out), oracle.sparse(q, k, v, ref_sel, case.scale),
+                          f"replay {it}")

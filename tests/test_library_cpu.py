@@ -179,3 +179,24 @@ def test_compute_calls_fail_closed_before_any_launch(da):
     # the dense plan handed to the sparse call
     assert lib.decode_attn_sparse(ctypes.byref(P), fake, fake, fake, fake, 8, fake, 0.1, 10, ws,
                                   P.workspace_bytes, None) == 1
+
+
+def test_selection_builder_fails_closed(da):
+    lib = da.library()
+    fake = ctypes.c_void_p(0x10000)
+    P = da.SelectProblem(4, 65408, 65408, 1920, 128, 65408, 2048)
+    call = lambda prob, s=fake, p=fake, o=fake: lib.decode_attn_build_selection(  # noqa: E731
+        ctypes.byref(prob), s, p, o, None)
+    assert call(P, p=None) == 1
+    assert call(P, o=None) == 1
+    assert call(P, s=None) == 1
+    assert call(P, o=ctypes.c_void_p(0x10002)) == 1
+    for field, bad in (("k_idx", 4097), ("k_idx", -1), ("batch", 0), ("topk", 0),
+                       ("score_stride", 100), ("window", -1), ("win_base", -5)):
+        Q = da.SelectProblem(4, 65408, 65408, 1920, 128, 65408, 2048)
+        setattr(Q, field, bad)
+        assert call(Q) == 1, field
+    big = da.SelectProblem(4, 131073, 131076, 1920, 128, 0, 2048)
+    assert call(big) == 2  # more candidates than the builder's row bitmap holds
+    odd = da.SelectProblem(4, 65407, 65407, 1920, 128, 0, 2048)
+    assert call(odd) == 1  # score rows must be a multiple of 4 floats apart
