@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--force-splits", type=int, default=0, help="dense split count (tuning)")
     ap.add_argument("--force-chunk", type=int, default=0,
                     help="keys (dense) or selection entries (sparse) per split (tuning)")
+    ap.add_argument("--with-append", action="store_true",
+                    help="dense: each step first appends the token's K/V rows at k_len - 1 "
+                         "(a whole decode step: append, then attend)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -293,11 +296,21 @@ def main():
         splits = plan.num_splits_max
     ws = da.workspace_for(plan)
 
+    append = args.with_append and not sparse
+    if append:
+        rng = np.random.Generator(np.random.PCG64(7))
+        kn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal((B, case.Hkv, 1, D), np.float32)))
+        vn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal((B, case.Hkv, 1, D), np.float32)))
+        pos_dev = torch.full((B,), case.k_len - 1, dtype=torch.int32, device="cuda")
+        algo_bytes += 2 * 2 * B * case.Hkv * D * 2  # new rows read and written
+
     def step(i):
         kk, vv = dks[i % sets], dvs[i % sets]
         if sparse:
             da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows, ws)
         else:
+            if append:
+                da.decode_attn_append_kv(kk, vv, kn, vn, pos_dev)
             da.decode_attn_dense(plan, dq, kk, vv, out, case.scale, case.k_len, ws)
 
     log(f"warmup {args.warmup} steps")
@@ -343,6 +356,8 @@ def main():
                 da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows,
                                       ws)
             else:
+                if append:
+                    da.decode_attn_append_kv(kk, vv, kn, vn, pos_dev)
                 da.decode_attn_dense_devlen(plan, dq, kk, vv, out, case.scale, klen_dev, ws)
 
         gstep(0)
@@ -388,7 +403,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(workload=desc, splits=splits, kv_sets=sets,
+        "config": dict(workload=desc + (" (+ KV append per step)" if append else ""),
+                       splits=splits, kv_sets=sets,
                        algorithmic_bytes_per_step=algo_bytes, **cfg),
         "roofline": {
             "bound": "hbm",

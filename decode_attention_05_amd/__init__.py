@@ -20,7 +20,7 @@ import os
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_sparse",
-    "decode_attn_build_selection", "SelectProblem",
+    "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
     "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
     "workspace_for",
     "EXPORTED_SYMBOLS",
@@ -32,7 +32,7 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
 EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
-                    "decode_attn_sparse", "decode_attn_build_selection",
+                    "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
 
@@ -74,6 +74,14 @@ class SelectProblem(ctypes.Structure):
     ]
 
 
+class AppendProblem(ctypes.Structure):
+    """Mirror of ``decode_attn_append_problem``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int64), ("window", ctypes.c_int32), ("win_base", ctypes.c_int64),
+    ]
+
+
 class DecodeAttnError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -106,6 +114,8 @@ def library():
         lib.decode_attn_sparse.restype = ctypes.c_int
         lib.decode_attn_build_selection.argtypes = [ctypes.POINTER(SelectProblem), P, P, P, P]
         lib.decode_attn_build_selection.restype = ctypes.c_int
+        lib.decode_attn_append_kv.argtypes = [ctypes.POINTER(AppendProblem), P, P, P, P, P, P]
+        lib.decode_attn_append_kv.restype = ctypes.c_int
         lib.decode_attn_set_timing_events.argtypes = [P, P]
         lib.decode_attn_set_timing_events.restype = ctypes.c_int
         lib.decode_attn_status_str.argtypes = [ctypes.c_int]
@@ -263,3 +273,20 @@ def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window
     _check(library().decode_attn_build_selection(ctypes.byref(prob), sp, pp, selp,
                                                  _stream_ptr(stream)))
     return sel
+
+
+def decode_attn_append_kv(k_cache, v_cache, k_new, v_new, pos, window: int = 0, win_base: int = 0,
+                          stream=None):
+    """Write token b's rows k_new/v_new [B,Hkv,1,D] into the caches [B,Hkv,capacity,D] at
+    row pos[b] (or win_base + pos[b] % window); ``pos`` is an int32 device tensor [B]."""
+    import torch
+    B, Hkv, cap, D = k_cache.shape
+    bf = torch.bfloat16
+    prob = AppendProblem(B, Hkv, D, cap, int(window), int(win_base))
+    args = (_tensor_ptr(k_cache, "k_cache", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v_cache, "v_cache", (B, Hkv, cap, D), bf),
+            _tensor_ptr(k_new, "k_new", (B, Hkv, 1, D), bf),
+            _tensor_ptr(v_new, "v_new", (B, Hkv, 1, D), bf),
+            _tensor_ptr(pos, "pos", (B,), torch.int32))
+    _check(library().decode_attn_append_kv(ctypes.byref(prob), *args, _stream_ptr(stream)))
+    return k_cache, v_cache

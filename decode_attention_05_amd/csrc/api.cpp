@@ -20,6 +20,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "append.h"
 #include "launch.h"
 #include "select.h"
 
@@ -422,6 +423,41 @@ decode_attn_status decode_attn_build_selection(const decode_attn_select_problem*
   const hipError_t e = da::launch_select(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(DA_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, void* k_cache,
+                                         void* v_cache, const void* k_new, const void* v_new,
+                                         const int32_t* pos, void* stream) {
+  if (!p) return fail(DA_ERR_INVALID_ARG, "problem pointer must be non-NULL");
+  if (p->batch < 1 || p->num_kv_heads < 1)
+    return fail(DA_ERR_INVALID_ARG, "batch and num_kv_heads must be >= 1");
+  if (p->head_dim < 8 || p->head_dim > 512 || p->head_dim % 8 != 0)
+    return fail(DA_ERR_INVALID_ARG, "head_dim must be a multiple of 8 in [8, 512], got %d",
+                p->head_dim);
+  if (p->capacity < 1) return fail(DA_ERR_INVALID_ARG, "capacity must be >= 1");
+  if (p->window < 0 || p->win_base < 0 || p->win_base + p->window > p->capacity)
+    return fail(DA_ERR_INVALID_ARG, "the window ring must lie inside [0, capacity)");
+  if (!k_cache || !v_cache || !k_new || !v_new || !pos)
+    return fail(DA_ERR_INVALID_ARG, "caches, new rows and pos must be non-NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+      ((uintptr_t)pos & 3u))
+    return fail(DA_ERR_INVALID_ARG, "caches and new rows must be 16-byte aligned, pos 4-byte");
+  da::AppendLaunch L{};
+  L.k_cache = static_cast<uint16_t*>(k_cache);
+  L.v_cache = static_cast<uint16_t*>(v_cache);
+  L.k_new = static_cast<const uint16_t*>(k_new);
+  L.v_new = static_cast<const uint16_t*>(v_new);
+  L.pos = pos;
+  L.B = p->batch;
+  L.Hkv = p->num_kv_heads;
+  L.D = p->head_dim;
+  L.capacity = p->capacity;
+  L.window = p->window;
+  L.win_base = p->win_base;
+  const hipError_t e = da::launch_append(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

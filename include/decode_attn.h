@@ -200,6 +200,35 @@ decode_attn_status decode_attn_build_selection(const decode_attn_select_problem*
                                                int32_t* sel, void* stream);
 
 /*
+ * KV append / window ring write: the current token's K and V rows go into the
+ * capacity cache before the attention call, at a row read on the device
+ * (fuel-dispatch page "DecodeFlashSpec", field k_len: the live length counts
+ * the new token; metrale page "AttnV41", decode_body: the window ring write at
+ * pos % window with the slot read on the device). Host struct.
+ */
+typedef struct {
+  int32_t batch;        /* B >= 1 tokens                                              */
+  int32_t num_kv_heads; /* Hkv >= 1                                                   */
+  int32_t head_dim;     /* D: a multiple of 8, at most 512                            */
+  int64_t capacity;     /* rows per (token, kv head) in the caches                    */
+  int32_t window;       /* 0: linear cache, row = pos; > 0: ring of `window` rows      */
+  int64_t win_base;     /* first row of the ring (window > 0); ring within capacity   */
+} decode_attn_append_problem;
+
+/*
+ * k_cache, v_cache [B, Hkv, capacity, D] bf16 (written); k_new, v_new
+ * [B, Hkv, 1, D] bf16; pos [B] int32 device positions. Token b's rows go to row
+ * pos[b] (window == 0) or win_base + pos[b] % window; a position that is
+ * negative or lands outside [0, capacity) writes nothing (device values are
+ * caller-owned, not validated on the host). One kernel on `stream`, no
+ * allocation, capturable. Pointers 16-byte aligned (pos 4-byte).
+ * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, void* k_cache,
+                                         void* v_cache, const void* k_new, const void* v_new,
+                                         const int32_t* pos, void* stream);
+
+/*
  * Diagnostics: time the split-K partial kernel (the kernel that streams K and V)
  * with caller-created HIP events. After this call, every compute call made on
  * the calling thread records `ev_before` on its stream immediately before

@@ -200,3 +200,20 @@ def test_selection_builder_fails_closed(da):
     assert call(big) == 2  # more candidates than the builder's row bitmap holds
     odd = da.SelectProblem(4, 65407, 65407, 1920, 128, 0, 2048)
     assert call(odd) == 1  # score rows must be a multiple of 4 floats apart
+
+
+def test_append_fails_closed(da):
+    lib = da.library()
+    fake = ctypes.c_void_p(0x10000)
+    call = lambda prob, kc=fake, pos=fake: lib.decode_attn_append_kv(  # noqa: E731
+        ctypes.byref(prob), kc, fake, fake, fake, pos, None)
+    good = da.AppendProblem(4, 8, 128, 4096, 0, 0)
+    assert call(good, kc=None) == 1
+    assert call(good, pos=None) == 1
+    assert call(good, kc=ctypes.c_void_p(0x10008)) == 1
+    assert call(good, pos=ctypes.c_void_p(0x10002)) == 1
+    for field, bad in (("head_dim", 12), ("head_dim", 1024), ("batch", 0), ("capacity", 0),
+                       ("window", -1), ("win_base", 4090)):
+        p = da.AppendProblem(4, 8, 128, 4096, 16 if field == "win_base" else 0, 0)
+        setattr(p, field, bad)
+        assert call(p) == 1, field
