@@ -126,3 +126,46 @@ def sparse(q, k, v, sel, scale: float, k_len: int | None = None, rows=None,
     if rc:
         raise ValueError(f"oracle_sparse failed with code {rc}")
     return out.reshape(B, Hq, 1, D) if r is None else out
+
+
+def dense_ragged(q, k, v, scale: float, k_lens, threads: int | None = None):
+    """Dense attention where sequence b attends rows [0, k_lens[b]) of its own
+    cache (a length of 0 gives zeros). The dense oracle, one sequence at a time."""
+    q = _bits(q, 4)
+    B, Hq, _, D = q.shape
+    out = np.zeros((B, Hq, 1, D), dtype=np.float64)
+    for b in range(B):
+        n = int(k_lens[b])
+        if n > 0:
+            out[b] = dense(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale, n, threads=threads)[0]
+    return out
+
+
+def unpage(pages, block_table, n_rows: int):
+    """Contiguous [B, Hkv, n_rows, D] cache from pages [num_pages, Hkv, page_size, D]
+    through block_table [B, max_pages]: logical row j of sequence b is row
+    j % page_size of page block_table[b, j // page_size]. Rows whose page entry is
+    negative are left as zeros (they lie past the sequence's length)."""
+    pages = np.asarray(pages)
+    num_pages, Hkv, page_size, D = pages.shape
+    B = block_table.shape[0]
+    out = np.zeros((B, Hkv, n_rows, D), dtype=pages.dtype)
+    for b in range(B):
+        for j0 in range(0, n_rows, page_size):
+            pg = int(block_table[b, j0 // page_size])
+            if pg < 0:
+                continue
+            n = min(page_size, n_rows - j0)
+            out[b, :, j0:j0 + n] = pages[pg, :, :n]
+    return out
+
+
+def dense_paged(q, k_pages, v_pages, block_table, scale: float, k_lens,
+                threads: int | None = None):
+    """Attention over a paged cache: the pages gathered into contiguous rows,
+    then the ragged dense oracle."""
+    page_size = k_pages.shape[2]
+    n_rows = block_table.shape[1] * page_size
+    k = unpage(k_pages, block_table, n_rows)
+    v = unpage(v_pages, block_table, n_rows)
+    return dense_ragged(q, k, v, scale, k_lens, threads=threads)
