@@ -77,6 +77,24 @@ def traffic_from_counters(workload: str):
 
 
 def build_inputs(args, torch, W, H):
+    if args.workload in W.RAGGED_CASES:
+        case = W.RAGGED_CASES[args.workload]
+        log(f"generating {args.workload} inputs (seed {case.seed})")
+        if case.page_size:
+            q, k, v, table, lens = W.paged_inputs(case)
+            layout = (f"paged cache of {k.shape[0]} pages x {case.page_size} rows, "
+                      f"block table [{case.B}, {case.max_pages}]")
+        else:
+            q, k, v, lens = W.ragged_inputs(case)
+            table = None
+            layout = f"contiguous cache, capacity {case.len_hi}"
+        host = dict(q=q, k=k, v=v, sel=None, lens=lens, table=table)
+        desc = (f"{case.name}: dense decode with one length per sequence, B={case.B} "
+                f"Hq={case.Hq} Hkv={case.Hkv} D={case.D}, lengths {int(lens.min())}.."
+                f"{int(lens.max())} (sum {int(lens.sum())}), {layout}")
+        cfg = dict(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
+                   max_k_len=case.len_hi, total_k_len=int(lens.sum()), page_size=case.page_size)
+        return case, host, 2 * k.nbytes, desc, cfg, case.algorithmic_bytes()
     if args.workload in W.DENSE_CASES:
         case = W.DENSE_CASES[args.workload]
         log(f"generating {args.workload} inputs (seed {case.seed})")
@@ -106,13 +124,29 @@ def cpu_baseline(args, case, host, algo_bytes, W):
     import oracle
     threads = oracle.default_threads()
     rows_total = case.B * case.Hq
+    ragged = "lens" in host
     # About one second of all-core work per probe; grow the sample to ~10 s of wall.
+    # Ragged batches sample every sequence equally (query row r is sequence r % B).
     n = min(rows_total, max(1, threads))
+    if ragged:
+        n = case.B * max(1, -(-n // case.B))
     t_probe = 0.0
     while True:
         rows = np.arange(n, dtype=np.int64) % rows_total
         t0 = time.perf_counter()
-        if host["sel"] is None:
+        if ragged:
+            flat = (rows % case.B) * case.Hq + (rows // case.B) % case.Hq
+            for b in range(case.B):
+                heads = flat[flat // case.Hq == b] % case.Hq
+                if host["table"] is not None:
+                    rows_b = int(host["table"].shape[1]) * case.page_size
+                    kb = oracle.unpage(host["k"], host["table"][b:b + 1], rows_b)
+                    vb = oracle.unpage(host["v"], host["table"][b:b + 1], rows_b)
+                else:
+                    kb, vb = host["k"][b:b + 1], host["v"][b:b + 1]
+                oracle.dense(host["q"][b:b + 1], kb, vb, case.scale, int(host["lens"][b]),
+                             rows=heads, threads=threads)
+        elif host["sel"] is None:
             oracle.dense(host["q"], host["k"], host["v"], case.scale, case.k_len, rows=rows,
                          threads=threads)
         else:
@@ -123,6 +157,8 @@ def cpu_baseline(args, case, host, algo_bytes, W):
             break
         grow = max(2.0, min(8.0, args.cpu_seconds / max(t_probe, 1e-3)))
         n = int(n * grow)
+        if ragged:
+            n = case.B * -(-n // case.B)
     per_step = t_probe * rows_total / n
     return {
         "value": round(algo_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -232,8 +268,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
-                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "select",
-                             "sparse_built"])
+                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
+                             "paged", "select", "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing of the plan-once call")
@@ -284,9 +320,25 @@ def main():
         dks.append(dks[0].clone())
         dvs.append(dvs[0].clone())
     dsel = H.to_dev_i32(host["sel"]) if sparse else None
+    ragged = "lens" in host
+    paged = ragged and host["table"] is not None
+    if ragged:
+        dlens = H.to_dev_i32(host["lens"])
+        dtable = H.to_dev_i32(host["table"]) if paged else None
     B, Hq, D = case.B, case.Hq, case.D
     out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
-    if sparse:
+    if ragged:
+        cap = case.len_hi
+        if paged:
+            plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap, page_size=case.page_size,
+                                       max_pages_per_seq=case.max_pages,
+                                       num_pages=host["k"].shape[0],
+                                       force_splits=args.force_splits)
+        else:
+            plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap,
+                                       force_splits=args.force_splits)
+        splits = plan.num_splits_max
+    elif sparse:
         plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.rows, topk_max=case.topk,
                                    kv_batch=case.kv_batch, force_chunk=args.force_chunk)
         splits = -(-case.topk // plan.chunk)
@@ -296,7 +348,7 @@ def main():
         splits = plan.num_splits_max
     ws = da.workspace_for(plan)
 
-    append = args.with_append and not sparse
+    append = args.with_append and not sparse and not ragged
     if append:
         rng = np.random.Generator(np.random.PCG64(7))
         kn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal((B, case.Hkv, 1, D), np.float32)))
@@ -306,7 +358,12 @@ def main():
 
     def step(i):
         kk, vv = dks[i % sets], dvs[i % sets]
-        if sparse:
+        if paged:
+            da.decode_attn_dense_paged(plan, dq, kk, vv, dtable, dlens, out, case.scale,
+                                       workspace=ws)
+        elif ragged:
+            da.decode_attn_dense_ragged(plan, dq, kk, vv, out, case.scale, dlens, workspace=ws)
+        elif sparse:
             da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows, ws)
         else:
             if append:
@@ -348,11 +405,14 @@ def main():
     # set once.
     graph_us = None
     if not args.no_graph:
-        klen_dev = torch.full((1,), 0 if sparse else case.k_len, dtype=torch.int32, device="cuda")
+        klen_dev = torch.full((1,), 0 if (sparse or ragged) else case.k_len, dtype=torch.int32,
+                              device="cuda")
 
         def gstep(i):
             kk, vv = dks[i % sets], dvs[i % sets]
-            if sparse:
+            if ragged:
+                step(i)
+            elif sparse:
                 da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows,
                                       ws)
             else:

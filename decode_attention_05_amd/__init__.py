@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
-    "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_sparse",
+    "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_dense_ragged",
+    "decode_attn_dense_paged", "decode_attn_sparse",
     "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
     "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
     "workspace_for",
@@ -32,6 +33,7 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
 EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
+                    "decode_attn_dense_ragged", "decode_attn_dense_paged",
                     "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
@@ -48,7 +50,8 @@ class Problem(ctypes.Structure):
         ("has_alibi", ctypes.c_int32), ("window_left", ctypes.c_int64),
         ("window_right", ctypes.c_int64), ("has_softcap", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-        ("force_chunk", ctypes.c_int32),
+        ("force_chunk", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -109,6 +112,13 @@ def library():
         lib.decode_attn_dense_devlen.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
                                                  P, P, ctypes.c_size_t, P]
         lib.decode_attn_dense_devlen.restype = ctypes.c_int
+        lib.decode_attn_dense_ragged.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
+                                                 P, ctypes.c_int32, P, ctypes.c_size_t, P]
+        lib.decode_attn_dense_ragged.restype = ctypes.c_int
+        lib.decode_attn_dense_paged.argtypes = [ctypes.POINTER(Plan), P, P, P, P, P,
+                                                ctypes.c_int32, P, ctypes.c_float, P,
+                                                ctypes.c_size_t, P]
+        lib.decode_attn_dense_paged.restype = ctypes.c_int
         lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
                                            ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_sparse.restype = ctypes.c_int
@@ -156,12 +166,14 @@ def decode_attn_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
                      kv_batch: int = 0, seq_q: int = 1, causal: bool = False,
                      has_alibi: bool = False, window_left: int = -1, window_right: int = -1,
                      has_softcap: bool = False, num_cus: int = 0, force_splits: int = 0,
-                     force_chunk: int = 0) -> Plan:
+                     force_chunk: int = 0, page_size: int = 0, max_pages_per_seq: int = 0,
+                     num_pages: int = 0) -> Plan:
     """Validate a problem and return its plan (see ``decode_attn_plan`` in the header)."""
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, seq_q, capacity,
                    capacity if max_k_len is None else max_k_len, topk_max, kv_batch,
                    int(bool(causal)), int(bool(has_alibi)), window_left, window_right,
-                   int(bool(has_softcap)), num_cus, force_splits, force_chunk)
+                   int(bool(has_softcap)), num_cus, force_splits, force_chunk, page_size,
+                   max_pages_per_seq, num_pages)
     plan = Plan()
     _check(library().decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)))
     return plan
@@ -236,6 +248,56 @@ def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_l
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense_devlen(ctypes.byref(plan), *args, float(softmax_scale),
                                               klen, ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def _lens_ptr(k_lens, B, stride):
+    import torch
+    if not (isinstance(k_lens, torch.Tensor) and k_lens.is_cuda and k_lens.dtype == torch.int32
+            and k_lens.is_contiguous()):
+        raise TypeError("k_lens must be a contiguous int32 device tensor")
+    if k_lens.numel() < (B - 1) * stride + 1:
+        raise ValueError(f"k_lens holds {k_lens.numel()} values, needs {(B - 1) * stride + 1}")
+    return k_lens.data_ptr()
+
+
+def decode_attn_dense_ragged(plan: Plan, q, k, v, out, softmax_scale: float, k_lens,
+                             k_lens_stride: int = 1, workspace=None, stream=None):
+    """Dense decode attention with sequence b's length k_lens[b * k_lens_stride] (device)."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    bf = torch.bfloat16
+    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    lens = _lens_ptr(k_lens, B, k_lens_stride)
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_dense_ragged(ctypes.byref(plan), *args, float(softmax_scale),
+                                              lens, int(k_lens_stride), ws, wsb,
+                                              _stream_ptr(stream)))
+    return out
+
+
+def decode_attn_dense_paged(plan: Plan, q, k_pages, v_pages, block_table, k_lens, out,
+                            softmax_scale: float, k_lens_stride: int = 1, workspace=None,
+                            stream=None):
+    """Dense decode attention over page pools [num_pages,Hkv,page_size,D] through
+    block_table [B, max_pages_per_seq] (int32, device)."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim
+    bf = torch.bfloat16
+    pool = (p.num_pages, Hkv, p.page_size, D)
+    qp = _tensor_ptr(q, "q", (B, Hq, 1, D), bf)
+    kp = _tensor_ptr(k_pages, "k_pages", pool, bf)
+    vp = _tensor_ptr(v_pages, "v_pages", pool, bf)
+    bt = _tensor_ptr(block_table, "block_table", (B, p.max_pages_per_seq), torch.int32)
+    lens = _lens_ptr(k_lens, B, k_lens_stride)
+    op = _tensor_ptr(out, "out", (B, Hq, 1, D), bf)
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_dense_paged(ctypes.byref(plan), qp, kp, vp, bt, lens,
+                                             int(k_lens_stride), op, float(softmax_scale), ws, wsb,
+                                             _stream_ptr(stream)))
     return out
 
 

@@ -92,7 +92,7 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 constexpr int kResidentPerCu = 2;
 constexpr int kMinChunk = 1024;
 constexpr int kMinSparseChunk = 128;
-constexpr int kKeyAlign = 16;
+constexpr int kKeyAlign = 32;  // the kernel's key tile: splits start on tile (and page) edges
 constexpr int kMaxSplits = 1 << 16;
 
 // Splits per unit that fill the resident slots once (1 when units >= CUs).
@@ -162,6 +162,18 @@ decode_attn_status validate_problem(const decode_attn_problem& p) {
     return fail(DA_ERR_INVALID_ARG, "kv_batch must be 0 or batch for a dense plan, got %d",
                 p.kv_batch);
   }
+  if (p.page_size != 0) {
+    if (p.topk_max > 0) return fail(DA_ERR_UNSUPPORTED, "page_size: paged caches are dense-only");
+    if (p.page_size < 32 || p.page_size % 32 != 0)
+      return fail(DA_ERR_INVALID_ARG, "page_size must be a positive multiple of 32, got %d",
+                  p.page_size);
+    if (p.max_pages_per_seq < 1 || p.num_pages < 1)
+      return fail(DA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (p.capacity != (int64_t)p.page_size * p.max_pages_per_seq)
+      return fail(DA_ERR_INVALID_ARG, "capacity must equal page_size * max_pages_per_seq");
+  }
+  if (p.force_chunk % 32 != 0 && p.page_size != 0)
+    return fail(DA_ERR_INVALID_ARG, "force_chunk must be a multiple of 32 for a paged plan");
   if (p.num_cus < 0 || p.force_splits < 0 || p.force_chunk < 0)
     return fail(DA_ERR_INVALID_ARG, "num_cus, force_splits and force_chunk must be >= 0");
   // The kernels address a KV row by a 32-bit byte offset inside one (batch, kv
@@ -254,6 +266,39 @@ decode_attn_status run(const da::PartialLaunch& L, void* stream) {
   return ok();
 }
 
+
+decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void* q,
+                                      const void* k, const void* v, const int32_t* block_table,
+                                      const int32_t* k_lens, int32_t k_lens_stride, void* out,
+                                      float softmax_scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  decode_attn_status s =
+      check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
+  if (s != DA_OK) return s;
+  const bool paged = block_table != nullptr;
+  if (paged != (plan->prob.page_size > 0))
+    return fail(DA_ERR_INVALID_ARG, paged ? "a paged call needs a plan with page_size > 0"
+                                          : "a paged plan needs decode_attn_dense_paged");
+  if (!k_lens) return fail(DA_ERR_INVALID_ARG, "k_lens must be non-NULL");
+  if (((uintptr_t)k_lens & 3u) || (paged && ((uintptr_t)block_table & 3u)))
+    return fail(DA_ERR_INVALID_ARG, "k_lens and block_table must be 4-byte aligned");
+  if (k_lens_stride < 1) return fail(DA_ERR_INVALID_ARG, "k_lens_stride must be >= 1");
+  const int S = plan->num_splits_max;
+  da::PartialLaunch L =
+      base_launch(*plan, q, k, v, out, softmax_scale, plan->prob.max_k_len, workspace, S);
+  L.k_len_dev = k_lens;
+  L.k_lens_stride = k_lens_stride;
+  L.chunk = plan->chunk;
+  L.sparse = false;
+  if (paged) {
+    L.block_table = block_table;
+    L.page_size = plan->prob.page_size;
+    L.max_pages = plan->prob.max_pages_per_seq;
+    L.num_pages = plan->prob.num_pages;
+  }
+  return run(L, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +361,8 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
   decode_attn_status s =
       check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
   if (s != DA_OK) return s;
+  if (plan->prob.page_size > 0)
+    return fail(DA_ERR_INVALID_ARG, "a paged plan needs decode_attn_dense_paged");
   if (k_len < 1 || k_len > plan->prob.max_k_len)
     return fail(DA_ERR_INVALID_ARG, "k_len must lie in [1, max_k_len = %lld], got %lld",
                 (long long)plan->prob.max_k_len, (long long)k_len);
@@ -341,6 +388,8 @@ decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, cons
   decode_attn_status s =
       check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
   if (s != DA_OK) return s;
+  if (plan->prob.page_size > 0)
+    return fail(DA_ERR_INVALID_ARG, "a paged plan needs decode_attn_dense_paged");
   if (!k_len_dev) return fail(DA_ERR_INVALID_ARG, "k_len_dev must be non-NULL");
   if (((uintptr_t)k_len_dev & 3u) != 0)
     return fail(DA_ERR_INVALID_ARG, "k_len_dev must be 4-byte aligned");
@@ -355,6 +404,26 @@ decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, cons
   if (log_enabled())
     std::fprintf(stderr, "[decode_attn] dense (device k_len) splits=%d\n", S);
   return run(L, stream);
+}
+
+decode_attn_status decode_attn_dense_ragged(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, const int32_t* k_lens,
+                                            int32_t k_lens_stride, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return dense_with_lengths(plan, q, k, v, nullptr, k_lens, k_lens_stride, out, softmax_scale,
+                            workspace, workspace_bytes, stream);
+}
+
+decode_attn_status decode_attn_dense_paged(const decode_attn_plan_t* plan, const void* q,
+                                           const void* k_pages, const void* v_pages,
+                                           const int32_t* block_table, const int32_t* k_lens,
+                                           int32_t k_lens_stride, void* out, float softmax_scale,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!block_table) return fail(DA_ERR_INVALID_ARG, "block_table must be non-NULL");
+  return dense_with_lengths(plan, q, k_pages, v_pages, block_table, k_lens, k_lens_stride, out,
+                            softmax_scale, workspace, workspace_bytes, stream);
 }
 
 decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void* q, const void* k,

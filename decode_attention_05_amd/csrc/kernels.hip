@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   int64_t chunk = a.chunk;
   if constexpr (!SPARSE) {
     if (a.k_len_dev) {
-      const int64_t raw = __builtin_amdgcn_readfirstlane(*a.k_len_dev);
+      const int64_t raw =
+          __builtin_amdgcn_readfirstlane(a.k_len_dev[(int64_t)b * a.k_lens_stride]);
       k_len = raw < 0 ? 0 : (raw > a.k_len ? a.k_len : raw);
       chunk = (k_len + a.S - 1) / a.S;
       chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
@@ -186,11 +187,29 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
     } else {
       const int64_t n = (tau < ntiles) ? j1 - kt : 0;
       R.mask = n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
-      // A tile past the end re-reads the split's last key (cached, never used).
-      const int64_t base = n > 0 ? kt : j1 - 1;
+      // A tile past the end re-reads the split's last key (cached, never used),
+      // or row 0 when the sequence is empty (k_len = 0 leaves j1 = 0).
+      const int64_t base = n > 0 ? kt : (j1 > 0 ? j1 - 1 : 0);
       last = n >= 32 ? 31 : (n > 0 ? (int)n - 1 : 0);
-      kb = kbytes + base * Gm::ROWB;
-      vb = vbytes + base * Gm::ROWB;
+      if (a.block_table) {
+        // Paged cache: a 32-key tile lies inside one page (tiles start at
+        // multiples of 32, pages hold a multiple of 32 rows). A page id outside
+        // [0, num_pages) is never read: the tile is dropped and its loads go to
+        // page 0.
+        const int64_t lp = base / a.page_size;
+        const int in_page = (int)(base - lp * a.page_size);
+        int64_t page = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + lp]);
+        if (page < 0 || page >= a.num_pages) {
+          page = 0;
+          R.mask = 0u;
+        }
+        const int64_t off = ((page * a.Hkv + hkv) * a.page_size + in_page) * Gm::ROWB;
+        kb = reinterpret_cast<const unsigned char*>(a.k) + off;
+        vb = reinterpret_cast<const unsigned char*>(a.v) + off;
+      } else {
+        kb = kbytes + base * Gm::ROWB;
+        vb = vbytes + base * Gm::ROWB;
+      }
     }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {

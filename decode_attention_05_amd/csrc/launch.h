@@ -12,8 +12,15 @@ struct PartialLaunch {
   const uint16_t* k;   // [kv_batch, Hkv, capacity, D] bf16
   const uint16_t* v;
   const int32_t* sel;  // sparse only: [B, topk]
-  const int32_t* k_len_dev;  // dense, optional: k_len read on the device (k_len then
-                             // holds its upper bound, the plan's max_k_len)
+  const int32_t* k_len_dev;  // dense, optional: live length(s) read on the device (k_len
+                             // then holds their upper bound, the plan's max_k_len)
+  int k_lens_stride;         // 0: one length for every sequence; else sequence b's length
+                             // is k_len_dev[b * k_lens_stride]
+  const int32_t* block_table;  // dense, optional: paged cache [B, max_pages] page ids;
+                               // k and v then point at pages [num_pages, Hkv, page_size, D]
+  int page_size;             // rows per page, a multiple of the 32-key tile
+  int max_pages;             // block-table row length
+  int64_t num_pages;
   uint16_t* out;       // [B, Hq, 1, D] bf16: written directly when S == 1
   float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1)
   float* part_m;       // [B*Hq, S] running max, base 2 (S > 1)

@@ -81,6 +81,10 @@ typedef struct {
   int32_t num_cus;      /* compute units to plan for; 0 = query the current HIP device    */
   int32_t force_splits; /* > 0: dense split count cap (tuning and tests); 0 = heuristic   */
   int32_t force_chunk;  /* > 0: keys (dense) or selection entries (sparse) per split      */
+  int32_t page_size;    /* 0: contiguous K/V; > 0: paged dense cache, a multiple of 32    */
+  int32_t max_pages_per_seq; /* paged: block-table row length; capacity must equal
+                                page_size * max_pages_per_seq                            */
+  int64_t num_pages;    /* paged: pages in the K and V page pools                         */
 } decode_attn_problem;
 
 /*
@@ -142,6 +146,45 @@ decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, cons
                                             float softmax_scale, const int32_t* k_len_dev,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
+
+/*
+ * Dense decode attention with one live length per sequence, read on the device
+ * (ragged batch; the DflashScratch page of metrale keeps one [kv_len, q_offset,
+ * q_rope_pos] u32 triple per band, read at kernel entry, so the lengths can be
+ * read straight out of such an array). Same arguments as decode_attn_dense
+ * except:
+ *   k_lens  device int32; sequence b attends rows [0, k_lens[b * k_lens_stride]).
+ *          Values are caller-owned: clamped to [0, max_k_len]; 0 gives zeros.
+ *   k_lens_stride  >= 1, in int32 elements (3 for the triples above).
+ * The launch is sized once for max_k_len (capturable, like
+ * decode_attn_dense_devlen). Returns as decode_attn_dense.
+ */
+decode_attn_status decode_attn_dense_ragged(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, const int32_t* k_lens,
+                                            int32_t k_lens_stride, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
+ * Dense decode attention over a paged KV cache (the DflashScratch page of
+ * metrale addresses its paged cache through slot indices). Needs a plan with
+ * page_size > 0.
+ *   k_pages, v_pages  [num_pages, Hkv, page_size, D] bf16 page pools.
+ *   block_table  device int32 [B, max_pages_per_seq]: logical row j of sequence b
+ *          is row j % page_size of page block_table[b, j / page_size]. Entries for
+ *          pages that cover [0, k_len_b) must be page ids in [0, num_pages); an id
+ *          outside that range is never read (those keys are skipped). Entries past
+ *          a sequence's length are ignored.
+ *   k_lens, k_lens_stride  as decode_attn_dense_ragged.
+ *   q, out, softmax_scale, workspace, stream  as decode_attn_dense.
+ * Returns as decode_attn_dense; DA_ERR_INVALID_ARG for a contiguous plan.
+ */
+decode_attn_status decode_attn_dense_paged(const decode_attn_plan_t* plan, const void* q,
+                                           const void* k_pages, const void* v_pages,
+                                           const int32_t* block_table, const int32_t* k_lens,
+                                           int32_t k_lens_stride, void* out, float softmax_scale,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
 
 /*
  * Index-selected sparse decode attention.

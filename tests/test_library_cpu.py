@@ -217,3 +217,52 @@ def test_append_fails_closed(da):
         p = da.AppendProblem(4, 8, 128, 4096, 16 if field == "win_base" else 0, 0)
         setattr(p, field, bad)
         assert call(p) == 1, field
+
+
+def paged_plan(da, **kw):
+    base = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, capacity=64 * 128,
+                page_size=64, max_pages_per_seq=128, num_pages=600, num_cus=256)
+    base.update(kw)
+    return da.decode_attn_plan(**base)
+
+
+def test_paged_plans(da):
+    p = paged_plan(da)
+    # chunks start on 32-key tiles, so with pages a multiple of 32 keys no tile crosses a page
+    assert p.prob.page_size == 64 and p.chunk % 32 == 0
+    for kw, status in ((dict(page_size=48), 1), (dict(page_size=16), 1),
+                       (dict(max_pages_per_seq=0), 1), (dict(num_pages=0), 1),
+                       (dict(capacity=64 * 128 + 32), 1), (dict(topk_max=16, kv_batch=4), 2),
+                       (dict(force_chunk=48), 1)):
+        with pytest.raises(da.DecodeAttnError) as ei:
+            paged_plan(da, **kw)
+        assert ei.value.status == status, kw
+
+
+def test_ragged_and_paged_fail_closed(da):
+    lib = da.library()
+    fake = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x20000)
+    P = plan(da)
+    G = paged_plan(da)
+    rag = lambda pl, lens=fake, stride=1, w=ws: lib.decode_attn_dense_ragged(  # noqa: E731
+        ctypes.byref(pl), fake, fake, fake, fake, 0.1, lens, stride, w, pl.workspace_bytes, None)
+    pag = lambda pl, bt=fake, lens=fake, stride=1: lib.decode_attn_dense_paged(  # noqa: E731
+        ctypes.byref(pl), fake, fake, fake, bt, lens, stride, fake, 0.1, ws, pl.workspace_bytes,
+        None)
+    assert rag(P, lens=None) == 1
+    assert rag(P, lens=ctypes.c_void_p(0x10002)) == 1
+    assert rag(P, stride=0) == 1
+    assert rag(P, w=None) == 3
+    assert rag(G) == 1                          # a paged plan needs the paged call
+    assert "paged" in da.decode_attn_last_error()
+    assert pag(P) == 1                          # a contiguous plan handed to the paged call
+    assert pag(G, bt=None) == 1
+    assert pag(G, bt=ctypes.c_void_p(0x10002)) == 1
+    assert pag(G, lens=None) == 1
+    assert pag(G, stride=-3) == 1
+    # the fixed-length calls refuse a paged plan
+    assert lib.decode_attn_dense(ctypes.byref(G), fake, fake, fake, fake, 0.1, 10, ws,
+                                 G.workspace_bytes, None) == 1
+    assert lib.decode_attn_dense_devlen(ctypes.byref(G), fake, fake, fake, fake, 0.1, fake, ws,
+                                        G.workspace_bytes, None) == 1

@@ -23,6 +23,9 @@ follows the metrale page "AttnV41", decode_fixed_topk and decode_prep):
                values with standard deviation 0.5
 * ``sparse``   B=4 Hq=64, one shared KV head of 65536 rows, D=128, topk 2048:
                128 window slots, then distinct random indices, then -1 pads
+* ``ragged``   B=32 Hq=32 Hkv=8 D=128, one live length per sequence: 32768
+               for sequence 0, log-uniform in [512, 32768] for the rest
+* ``paged``    the same lengths over a paged cache of 64-row pages, shuffled
 """
 
 from __future__ import annotations
@@ -217,6 +220,105 @@ def sparse_inputs(case: SparseCase, seed: int | None = None):
     sel = selection(np.random.Generator(np.random.PCG64(ss)), case.B, case.rows, case.topk,
                     case.window, case.counts)
     return q, k, v, sel
+
+
+@dataclass
+class RaggedCase:
+    """A batch whose sequences have different live lengths.
+
+    Sequence 0 has the longest length ``len_hi``; the others are drawn
+    log-uniformly from [len_lo, len_hi]. With ``page_size`` > 0 the cache is
+    paged: one pool of pages [num_pages, Hkv, page_size, D] per K and V, each
+    sequence holding ceil(len / page_size) distinct pages at shuffled positions
+    of the pool, -1 in its block-table row past its length.
+    """
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    len_lo: int
+    len_hi: int             # also the capacity (rows per sequence) of the plan
+    scale: float
+    page_size: int = 0
+    std: float = 1.0
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.len_hi // self.page_size)
+
+    def lengths(self) -> np.ndarray:
+        return ragged_lengths(seeds(self.seed)[3], self.B, self.len_lo, self.len_hi)
+
+    def algorithmic_bytes(self) -> int:
+        """Live K+V rows of every sequence plus q and out (plus the block table if paged)."""
+        n = int(self.lengths().sum())
+        extra = self.B * self.max_pages * 4 if self.page_size else 0
+        return 2 * n * self.Hkv * self.D * 2 + 2 * (self.B * self.Hq * self.D * 2) + extra
+
+
+RAGGED_CASES = {
+    "ragged": RaggedCase("ragged", 32, 32, 8, 128, 512, 32768, _f32(1.0 / math.sqrt(128)),
+                         seed=6),
+    "paged": RaggedCase("paged", 32, 32, 8, 128, 512, 32768, _f32(1.0 / math.sqrt(128)),
+                        page_size=64, seed=6),
+}
+
+
+def ragged_lengths(seed: np.random.SeedSequence, B: int, lo: int, hi: int) -> np.ndarray:
+    """int32 [B]: hi for sequence 0, then log-uniform integers in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = np.exp(rng.uniform(math.log(lo), math.log(hi + 1), size=B))
+    lens = np.clip(np.floor(x), lo, hi).astype(np.int32)
+    lens[0] = hi
+    return lens
+
+
+def page_table(rng: np.random.Generator, lens, page_size: int, max_pages: int,
+               spare: int = 0):
+    """Block table [B, max_pages] int32 and the pool size.
+
+    Sequence b needs ceil(lens[b] / page_size) pages; all pages of all
+    sequences (plus ``spare`` unused ones) are one shuffled pool, handed out in
+    a random order. Entries past a sequence's pages are -1.
+    """
+    need = [-(-int(n) // page_size) for n in lens]
+    if max(need, default=0) > max_pages:
+        raise ValueError("a sequence needs more pages than a block-table row holds")
+    num_pages = sum(need) + spare
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((len(lens), max_pages), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    return table, num_pages
+
+
+def ragged_inputs(case: RaggedCase, seed: int | None = None):
+    """Contiguous layout: q [B,Hq,1,D], k, v [B,Hkv,len_hi,D], lengths [B] int32."""
+    sq, sk, sv, sl = seeds(case.seed if seed is None else seed)
+    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    k = normal_bf16(sk, (case.B, case.Hkv, case.len_hi, case.D), case.std)
+    v = normal_bf16(sv, (case.B, case.Hkv, case.len_hi, case.D), case.std)
+    return q, k, v, ragged_lengths(sl, case.B, case.len_lo, case.len_hi)
+
+
+def paged_inputs(case: RaggedCase, seed: int | None = None, spare: int = 0):
+    """Paged layout: q [B,Hq,1,D], k_pages, v_pages [num_pages,Hkv,page_size,D],
+    block table [B, max_pages] int32, lengths [B] int32."""
+    sq, sk, sv, sl = seeds(case.seed if seed is None else seed)
+    lens = ragged_lengths(sl, case.B, case.len_lo, case.len_hi)
+    table, num_pages = page_table(np.random.Generator(np.random.PCG64(sl.spawn(1)[0])), lens,
+                                  case.page_size, case.max_pages, spare)
+    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    pool = (num_pages, case.Hkv, case.page_size, case.D)
+    return q, normal_bf16(sk, pool, case.std), normal_bf16(sv, pool, case.std), table, lens
 
 
 def random_case(seed: int, B: int, Hq: int, Hkv: int, D: int, cap: int, std: float = 1.0):
