@@ -335,9 +335,9 @@ def main():
                                        num_pages=host["k"].shape[0],
                                        force_splits=args.force_splits)
         else:
-            plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap,
+            plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap, ragged=True,
                                        force_splits=args.force_splits)
-        splits = plan.num_splits_max
+        splits = plan.balanced_wgs
     elif sparse:
         plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.rows, topk_max=case.topk,
                                    kv_batch=case.kv_batch, force_chunk=args.force_chunk)

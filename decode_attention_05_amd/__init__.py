@@ -52,6 +52,7 @@ class Problem(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
         ("force_chunk", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+        ("ragged", ctypes.c_int32),
     ]
 
 
@@ -60,7 +61,7 @@ class Plan(ctypes.Structure):
     _fields_ = [
         ("prob", Problem), ("group", ctypes.c_int32), ("num_splits_max", ctypes.c_int32),
         ("chunk", ctypes.c_int32), ("num_cus", ctypes.c_int32), ("kind", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+        ("balanced_wgs", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
     ]
 
     @property
@@ -167,13 +168,13 @@ def decode_attn_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
                      has_alibi: bool = False, window_left: int = -1, window_right: int = -1,
                      has_softcap: bool = False, num_cus: int = 0, force_splits: int = 0,
                      force_chunk: int = 0, page_size: int = 0, max_pages_per_seq: int = 0,
-                     num_pages: int = 0) -> Plan:
+                     num_pages: int = 0, ragged: bool = False) -> Plan:
     """Validate a problem and return its plan (see ``decode_attn_plan`` in the header)."""
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, seq_q, capacity,
                    capacity if max_k_len is None else max_k_len, topk_max, kv_batch,
                    int(bool(causal)), int(bool(has_alibi)), window_left, window_right,
                    int(bool(has_softcap)), num_cus, force_splits, force_chunk, page_size,
-                   max_pages_per_seq, num_pages)
+                   max_pages_per_seq, num_pages, int(bool(ragged)))
     plan = Plan()
     _check(library().decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)))
     return plan

@@ -162,6 +162,10 @@ decode_attn_status validate_problem(const decode_attn_problem& p) {
     return fail(DA_ERR_INVALID_ARG, "kv_batch must be 0 or batch for a dense plan, got %d",
                 p.kv_batch);
   }
+  if (p.ragged != 0 && p.ragged != 1)
+    return fail(DA_ERR_INVALID_ARG, "ragged must be 0 or 1, got %d", p.ragged);
+  if (p.ragged && p.topk_max > 0)
+    return fail(DA_ERR_UNSUPPORTED, "ragged: per-sequence lengths are dense-only");
   if (p.page_size != 0) {
     if (p.topk_max > 0) return fail(DA_ERR_UNSUPPORTED, "page_size: paged caches are dense-only");
     if (p.page_size < 32 || p.page_size % 32 != 0)
@@ -223,6 +227,12 @@ uint64_t workspace_for(const decode_attn_problem& p, int S) {
   return (uint64_t)p.batch * p.num_q_heads * (uint64_t)S * (p.head_dim + 2) * sizeof(float);
 }
 
+// Length-balanced schedule: two partial slots of heads_per_wg rows per workgroup.
+uint64_t balanced_workspace(const decode_attn_plan_t& P) {
+  return (uint64_t)P.balanced_wgs * 2 * heads_per_wg(P.group) * (P.prob.head_dim + 2) *
+         sizeof(float);
+}
+
 decode_attn_status check_common(const decode_attn_plan_t* plan, int kind, const void* q,
                                 const void* k, const void* v, void* out, float scale,
                                 void* workspace, size_t workspace_bytes) {
@@ -279,24 +289,46 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
   if (paged != (plan->prob.page_size > 0))
     return fail(DA_ERR_INVALID_ARG, paged ? "a paged call needs a plan with page_size > 0"
                                           : "a paged plan needs decode_attn_dense_paged");
+  if (plan->balanced_wgs < 1 || plan->workspace_bytes < balanced_workspace(*plan))
+    return fail(DA_ERR_INVALID_ARG, "per-sequence lengths need a plan made with ragged = 1");
   if (!k_lens) return fail(DA_ERR_INVALID_ARG, "k_lens must be non-NULL");
   if (((uintptr_t)k_lens & 3u) || (paged && ((uintptr_t)block_table & 3u)))
     return fail(DA_ERR_INVALID_ARG, "k_lens and block_table must be 4-byte aligned");
   if (k_lens_stride < 1) return fail(DA_ERR_INVALID_ARG, "k_lens_stride must be >= 1");
-  const int S = plan->num_splits_max;
   da::PartialLaunch L =
-      base_launch(*plan, q, k, v, out, softmax_scale, plan->prob.max_k_len, workspace, S);
+      base_launch(*plan, q, k, v, out, softmax_scale, plan->prob.max_k_len, nullptr, 1);
   L.k_len_dev = k_lens;
   L.k_lens_stride = k_lens_stride;
-  L.chunk = plan->chunk;
   L.sparse = false;
+  L.balanced_wgs = plan->balanced_wgs;
+  const int64_t slots = (int64_t)plan->balanced_wgs * 2 * L.heads_per_wg;
+  float* ws = static_cast<float*>(workspace);
+  L.part_o = ws;
+  L.part_m = ws + slots * plan->prob.head_dim;
+  L.part_l = L.part_m + slots;
   if (paged) {
     L.block_table = block_table;
     L.page_size = plan->prob.page_size;
     L.max_pages = plan->prob.max_pages_per_seq;
     L.num_pages = plan->prob.num_pages;
   }
-  return run(L, stream);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_ev_before) {
+    e = hipEventRecord(g_ev_before, st);
+    if (e != hipSuccess) return fail(DA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
+  e = da::launch_balanced(L, st);
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "balanced kernel launch failed: %s", hipGetErrorString(e));
+  if (g_ev_after) {
+    e = hipEventRecord(g_ev_after, st);
+    if (e != hipSuccess) return fail(DA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
+  e = da::launch_balanced_combine(L, st);
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "balanced combine launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // namespace
@@ -344,6 +376,11 @@ decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_pl
   }
   if (P.num_splits_max > kMaxSplits) return fail(DA_ERR_INVALID_ARG, "too many splits");
   P.workspace_bytes = workspace_for(P.prob, P.num_splits_max);
+  if (P.kind == 0 && (p->ragged || p->page_size > 0)) {
+    P.prob.ragged = 1;
+    P.balanced_wgs = kResidentPerCu * cus;
+    P.workspace_bytes = std::max(P.workspace_bytes, balanced_workspace(P));
+  }
   if (log_enabled())
     std::fprintf(stderr,
                  "[decode_attn] plan kind=%s B=%d Hq=%d Hkv=%d D=%d G=%d heads/wg=%d units=%lld "

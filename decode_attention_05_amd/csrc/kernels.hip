@@ -96,31 +96,45 @@ struct TileRegs {
   uint32_t mask;                 // bit i: key i of the tile is valid
 };
 
+// Where attend_range leaves the result of its GT heads: the bf16 output rows
+// (direct: head hh at out + hh * D), or fp32 unnormalised partials with their
+// running max (base 2) and denominator (head hh at po + hh * po_stride and
+// pm / pl + hh * pm_stride).
+struct RangeOut {
+  bool direct;
+  uint16_t* out;
+  float* po;
+  float* pm;
+  float* pl;
+  int64_t po_stride;
+  int64_t pm_stride;
+};
+
+// The whole workgroup attends the GT query heads h0 .. h0 + GT - 1 of sequence
+// b (kv head hkv) over keys [j0, j1) of its KV stream (dense: rows of the cache;
+// sparse: entries of the selection), k_len bounding the usable rows, and
+// writes the merged result of its four waves to `ro`. Every thread of the
+// workgroup must call it with the same arguments; it synchronises the
+// workgroup and uses all of `lds`, so a caller that calls it again first
+// synchronises.
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
+__device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned char* lds,
+                                             float (&mrg_m)[kWaves][16],
+                                             float (&mrg_l)[kWaves][16], int b, int hkv, int h0,
+                                             int GT, int64_t k_len, int64_t j0, int64_t j1,
+                                             const RangeOut& ro) {
   using Gm = Geometry<D>;
   constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
-  __shared__ float mrg_m[kWaves][16];
-  __shared__ float mrg_l[kWaves][16];
-
-  const int tid = threadIdx.x;
+  // Opaque copy of the thread id: the per-lane offsets derived from it are
+  // rebuilt in each call rather than hoisted out of a caller's loop (where they
+  // would stay live, and spill, across calls).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar addressing
   const int g = lane >> 4;   // lane group: which 8 bf16 of a 32-wide k slice
   const int r16 = lane & 15; // A-operand row / C-operand column
-
-  // Workgroup coordinates: split fastest, then head tile, then (b, kv head).
-  const int GT = a.heads_per_wg;
-  const int tiles_h = a.G / GT;
-  int wg = blockIdx.x;
-  const int s = wg % a.S;
-  wg /= a.S;
-  const int ht = wg % tiles_h;
-  const int bh = wg / tiles_h;
-  const int b = bh / a.Hkv, hkv = bh % a.Hkv;
-  const int h0 = hkv * a.G + ht * GT;  // first query head of this tile
 
   // B operand of S^T = K Q^T: lane holds q[h0 + r16][8 (4c + g) .. + 7].
   bf16x8 qop[NC];
@@ -138,26 +152,6 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   const uint4* __restrict__ kp = reinterpret_cast<const uint4*>(a.k + kv_base);
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(a.v + kv_base);
 
-  // Live length and split size. With a device-resident length (plan-once
-  // decode) the S splits share [0, k_len) evenly for whatever k_len the device
-  // holds; a value outside [0, max_k_len] is clamped, and k_len = 0 yields zeros.
-  int64_t k_len = a.k_len;
-  int64_t chunk = a.chunk;
-  if constexpr (!SPARSE) {
-    if (a.k_len_dev) {
-      const int64_t raw =
-          __builtin_amdgcn_readfirstlane(a.k_len_dev[(int64_t)b * a.k_lens_stride]);
-      k_len = raw < 0 ? 0 : (raw > a.k_len ? a.k_len : raw);
-      chunk = (k_len + a.S - 1) / a.S;
-      chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
-      if (chunk == 0) chunk = kTileKeys;
-    }
-  }
-
-  // This split: keys (dense) or selection entries (sparse) [j0, j1).
-  const int64_t j0 = (int64_t)s * chunk;
-  const int64_t j_end = SPARSE ? (int64_t)a.topk : k_len;
-  const int64_t j1 = (j0 + chunk < j_end) ? j0 + chunk : j_end;
   const int ntiles = (j1 > j0) ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
   const int32_t* sel_row = SPARSE ? a.sel + (int64_t)b * a.topk : nullptr;
 
@@ -179,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
     if constexpr (SPARSE) {
       const int64_t t = kt + (lane & 31);
       const int32_t r = (tau < ntiles && t < j1) ? sel_row[t] : -1;
-      const bool ok = r >= 0 && (int64_t)r < a.k_len;
+      const bool ok = r >= 0 && (int64_t)r < k_len;
       row_lane = ok ? (int)r : 0;
       R.mask = (uint32_t)__ballot(ok);
       kb = kbytes;
@@ -371,27 +365,303 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
       for (int e = 0; e < PER; ++e) acc[e] = acc[e] * wa + src[e] * wb;
       M = Mn;
     }
-    const int64_t row = (int64_t)b * a.Hq + h0 + hh;
-    if (a.S == 1) {
+    if (ro.direct) {
       const float inv = (L > 0.f) ? 1.f / L : 0.f;
       uint32_t w4[PER / 2];
 #pragma unroll
       for (int e = 0; e < PER / 2; ++e) w4[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      uint16_t* dst = ro.out + (int64_t)hh * D + d0;
       if constexpr (PER == 8)
-        *reinterpret_cast<uint4*>(a.out + row * D + d0) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       else
-        *reinterpret_cast<uint2*>(a.out + row * D + d0) = make_uint2(w4[0], w4[1]);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w4[0], w4[1]);
     } else {
-      float* po = a.part_o + (row * a.S + s) * D + d0;
+      float* po = ro.po + hh * ro.po_stride + d0;
 #pragma unroll
       for (int e = 0; e < PER; e += 4)
         *reinterpret_cast<float4*>(po + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
       if (d0 == 0) {
-        a.part_m[row * a.S + s] = M;
-        a.part_l[row * a.S + s] = L;
+        ro.pm[hh * ro.pm_stride] = M;
+        ro.pl[hh * ro.pm_stride] = L;
       }
     }
   }
+}
+
+// Split-K pass: one workgroup per (batch, kv head, head tile, split), split
+// fastest. Writes the bf16 output directly when the plan does not split (S = 1).
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
+  using Gm = Geometry<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
+
+  const int GT = a.heads_per_wg;
+  const int tiles_h = a.G / GT;
+  int wg = blockIdx.x;
+  const int s = wg % a.S;
+  wg /= a.S;
+  const int ht = wg % tiles_h;
+  const int bh = wg / tiles_h;
+  const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+  const int h0 = hkv * a.G + ht * GT;  // first query head of this tile
+
+  // Live length and split size. With a device-resident length (plan-once
+  // decode) the S splits share [0, k_len) evenly for whatever k_len the device
+  // holds; a value outside [0, max_k_len] is clamped, and k_len = 0 yields zeros.
+  int64_t k_len = a.k_len;
+  int64_t chunk = a.chunk;
+  if constexpr (!SPARSE) {
+    if (a.k_len_dev) {
+      const int64_t raw =
+          __builtin_amdgcn_readfirstlane(a.k_len_dev[(int64_t)b * a.k_lens_stride]);
+      k_len = raw < 0 ? 0 : (raw > a.k_len ? a.k_len : raw);
+      chunk = (k_len + a.S - 1) / a.S;
+      chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+      if (chunk == 0) chunk = kTileKeys;
+    }
+  }
+
+  // This split: keys (dense) or selection entries (sparse) [j0, j1).
+  const int64_t j0 = (int64_t)s * chunk;
+  const int64_t j_end = SPARSE ? (int64_t)a.topk : k_len;
+  const int64_t j1 = (j0 + chunk < j_end) ? j0 + chunk : j_end;
+
+  const int64_t row0 = (int64_t)b * a.Hq + h0;
+  RangeOut ro;
+  ro.direct = a.S == 1;
+  ro.out = a.out + row0 * D;
+  ro.po = a.S > 1 ? a.part_o + (row0 * a.S + s) * D : nullptr;
+  ro.pm = a.S > 1 ? a.part_m + row0 * a.S + s : nullptr;
+  ro.pl = a.S > 1 ? a.part_l + row0 * a.S + s : nullptr;
+  ro.po_stride = (int64_t)a.S * D;
+  ro.pm_stride = a.S;
+  attend_range<D, SPARSE>(a, lds, mrg_m, mrg_l, b, hkv, h0, GT, k_len, j0, j1, ro);
+}
+
+// --- length-balanced schedule (one live length per sequence) ----------------
+//
+// Key streams: one per (sequence b, kv head, head tile), of tiles_of(len_b)
+// 32-key tiles, laid end to end in the order b, then kv head, then head tile.
+// Workgroup w takes tiles [w * per_wg, (w + 1) * per_wg) of that concatenation,
+// so every workgroup streams the same number of tiles whatever the mix of
+// lengths. A stream that lies inside one workgroup's run is finished there
+// (bf16 output); a stream cut by a run boundary leaves one fp32 partial per
+// workgroup that touches it, in slot 0 of the workgroup (the first stream of
+// its run) or slot 1 (the last), and the combine merges them. Both kernels
+// derive the schedule from the lengths alone, with the same integer
+// arithmetic.
+
+constexpr int64_t kMinTilesPerWg = 8;
+
+__device__ __forceinline__ int64_t seq_len(const PartialLaunch& a, int b) {
+  const int64_t raw = a.k_len_dev[(int64_t)b * a.k_lens_stride];
+  return raw < 0 ? 0 : (raw > a.k_len ? a.k_len : raw);
+}
+
+__device__ __forceinline__ int64_t tiles_of(int64_t len) {
+  return (len + kTileKeys - 1) / kTileKeys;
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// A value known to be equal in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct Schedule {
+  int64_t total;   // tiles over all streams
+  int64_t per_wg;  // tiles per workgroup run
+};
+
+// Every lane of the calling wave gets the same schedule.
+__device__ __forceinline__ Schedule balanced_schedule(const PartialLaunch& a, int streams_per_seq) {
+  const int lane = threadIdx.x & 63;
+  int64_t mine = 0;
+  for (int base = 0; base < a.B; base += 64)
+    if (base + lane < a.B) mine += tiles_of(seq_len(a, base + lane));
+  Schedule sc;
+  sc.total = uniform_i64(wave_sum_i64(mine)) * streams_per_seq;
+  const int64_t even = (sc.total + a.balanced_wgs - 1) / a.balanced_wgs;
+  sc.per_wg = even > kMinTilesPerWg ? even : kMinTilesPerWg;
+  return sc;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) {
+  using Gm = Geometry<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  const int GT = a.heads_per_wg;
+  const int tiles_h = a.G / GT;
+  const int per_seq = a.Hkv * tiles_h;  // streams per sequence
+  const Schedule sc = balanced_schedule(a, per_seq);
+  const int64_t t0 = (int64_t)blockIdx.x * sc.per_wg;
+  if (t0 >= sc.total) return;  // the whole workgroup leaves together
+  const int64_t t1 = (t0 + sc.per_wg < sc.total) ? t0 + sc.per_wg : sc.total;
+
+  // The sequence whose streams hold tile t0: the first b with
+  // per_seq * (tiles before b) <= t0 < per_seq * (tiles up to b). 64 sequences
+  // per step, lane-parallel inclusive scan.
+  int b = 0;
+  int64_t seq_start = 0;  // first tile of sequence b's streams
+  {
+    int64_t run = 0;
+    for (int base = 0; base < a.B; base += 64) {
+      const int64_t n = (base + lane < a.B) ? tiles_of(seq_len(a, base + lane)) * per_seq : 0;
+      int64_t inc = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      inc += run;
+      const int64_t exc = inc - n;
+      const uint64_t hit = __ballot(n > 0 && exc <= t0 && t0 < inc);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        b = base + src;
+        seq_start = uniform_i64(__shfl(exc, src));
+        break;
+      }
+      run = uniform_i64(__shfl(inc, 63));
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  int64_t len = __builtin_amdgcn_readfirstlane(seq_len(a, b));
+  int64_t nb = tiles_of(len);  // tiles of each stream of sequence b
+  if (nb == 0) return;         // unreachable: t0 < total lies in a non-empty sequence
+  const int64_t rel = t0 - seq_start;
+  int r = (int)(rel / nb);     // stream of sequence b: kv head * tiles_h + head tile
+  int64_t jt = rel - (int64_t)r * nb;
+  int64_t x = t0;
+  for (;;) {
+    const int64_t left = t1 - x;
+    const int64_t nt = (nb - jt < left) ? nb - jt : left;
+    const int hkv = r / tiles_h, ht = r % tiles_h;
+    const int h0 = hkv * a.G + ht * GT;
+    RangeOut ro;
+    ro.direct = (jt == 0 && nt == nb);  // the whole stream is in this run
+    ro.out = a.out + ((int64_t)b * a.Hq + h0) * D;
+    const int64_t slot = ((int64_t)blockIdx.x * 2 + (x == t0 ? 0 : 1)) * GT;
+    ro.po = a.part_o + slot * D;
+    ro.pm = a.part_m + slot;
+    ro.pl = a.part_l + slot;
+    ro.po_stride = D;
+    ro.pm_stride = 1;
+    const int64_t j1 = (jt + nt) * kTileKeys;
+    attend_range<D, false>(a, lds, mrg_m, mrg_l, b, hkv, h0, GT, len, jt * kTileKeys,
+                           j1 < len ? j1 : len, ro);
+    x += nt;
+    if (x >= t1) break;
+    __syncthreads();  // the merge area is read before the next range's V tiles land there
+    // Next stream: the next head tile / kv head, else the next non-empty sequence.
+    jt = 0;
+    if (++r == per_seq) {
+      r = 0;
+      if (b + 1 >= a.B) break;  // unreachable: tiles remain before t1 <= total
+      do {
+        ++b;
+        len = __builtin_amdgcn_readfirstlane(seq_len(a, b));
+        nb = tiles_of(len);
+      } while (nb == 0 && b + 1 < a.B);
+      if (nb == 0) break;  // unreachable: tiles remain before t1 <= total
+    }
+  }
+}
+
+// Merge of the partials of one stream (b, kv head, head tile) cut by the
+// balanced schedule; one workgroup per stream, thread t owns head t / 16 and
+// D/16 values. Streams inside one run were finished by attend_balanced and are
+// left alone; an empty sequence gets zeros. Partials are merged in run order
+// with weights 2^(m - M).
+template <int D>
+__global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
+  constexpr int PER = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int GT = a.heads_per_wg;
+  const int tiles_h = a.G / GT;
+  const int per_seq = a.Hkv * tiles_h;
+  const int b = blockIdx.x / per_seq, r = blockIdx.x % per_seq;
+  const int h0 = (r / tiles_h) * a.G + (r % tiles_h) * GT;
+  const int hh = tid >> 4, t16 = tid & 15, d0 = t16 * PER;
+  uint16_t* out = a.out + ((int64_t)b * a.Hq + h0 + hh) * D + d0;
+
+  // One pass over the lengths: all tiles (the schedule) and the tiles before b.
+  int64_t all = 0, before = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int bb = base + lane;
+    const int64_t n = bb < a.B ? tiles_of(seq_len(a, bb)) : 0;
+    all += n;
+    before += bb < b ? n : 0;
+  }
+  const int64_t total = uniform_i64(wave_sum_i64(all)) * per_seq;
+  const int64_t even = (total + a.balanced_wgs - 1) / a.balanced_wgs;
+  const int64_t per_wg = even > kMinTilesPerWg ? even : kMinTilesPerWg;
+  const int64_t nb = tiles_of(seq_len(a, b));
+  if (nb == 0) {
+    if (hh < GT) {
+      if constexpr (PER == 8)
+        *reinterpret_cast<uint4*>(out) = make_uint4(0u, 0u, 0u, 0u);
+      else
+        *reinterpret_cast<uint2*>(out) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  const int64_t ts = uniform_i64(wave_sum_i64(before)) * per_seq + (int64_t)r * nb;
+  const int64_t ws = ts / per_wg, we = (ts + nb - 1) / per_wg;
+  if (ws == we || hh >= GT) return;
+
+  auto slot_of = [&](int64_t w) -> int64_t {
+    const int first = (w > ws || ts == w * per_wg) ? 0 : 1;
+    return (w * 2 + first) * GT + hh;
+  };
+  // M over the pieces: the 16 threads of a head take every 16th piece.
+  float M = kNegInf;
+  for (int64_t w = ws + t16; w <= we; w += 16) M = fmaxf(M, a.part_m[slot_of(w)]);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float L = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int64_t w = ws; w <= we; ++w) {
+      const int64_t sl = slot_of(w);
+      const float mw = a.part_m[sl];
+      const float wt = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+      L += a.part_l[sl] * wt;
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + sl * D + d0);
+#pragma unroll
+      for (int e = 0; e < PER / 4; ++e) {
+        const float4 o = src[e];
+        acc[4 * e] += o.x * wt;
+        acc[4 * e + 1] += o.y * wt;
+        acc[4 * e + 2] += o.z * wt;
+        acc[4 * e + 3] += o.w * wt;
+      }
+    }
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  uint32_t w4[PER / 2];
+#pragma unroll
+  for (int e = 0; e < PER / 2; ++e) w4[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  if constexpr (PER == 8)
+    *reinterpret_cast<uint4*>(out) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  else
+    *reinterpret_cast<uint2*>(out) = make_uint2(w4[0], w4[1]);
 }
 
 // Log-sum-exp merge of the S split partials of one output row per workgroup.
@@ -467,7 +737,42 @@ hipError_t launch_partial_d(const PartialLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_balanced_d(const PartialLaunch& L, hipStream_t stream) {
+  hipLaunchKernelGGL(attend_balanced<D>, dim3((unsigned)L.balanced_wgs), dim3(kThreads), 0, stream,
+                     L);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_balanced_combine_d(const PartialLaunch& L, hipStream_t stream) {
+  const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
+  hipLaunchKernelGGL(combine_balanced<D>, dim3((unsigned)streams), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
+
+bool balanced_ok(const PartialLaunch& L) {
+  const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
+  return !L.sparse && L.k_len_dev && L.balanced_wgs > 0 && L.heads_per_wg >= 1 &&
+         L.heads_per_wg <= 16 && streams > 0 && streams <= 0x7fffffff && L.part_o && L.part_m &&
+         L.part_l;
+}
+
 }  // namespace
+
+hipError_t launch_balanced(const PartialLaunch& L, hipStream_t stream) {
+  if (!balanced_ok(L)) return hipErrorInvalidConfiguration;
+  if (L.D == 128) return launch_balanced_d<128>(L, stream);
+  if (L.D == 64) return launch_balanced_d<64>(L, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_balanced_combine(const PartialLaunch& L, hipStream_t stream) {
+  if (!balanced_ok(L)) return hipErrorInvalidConfiguration;
+  if (L.D == 128) return launch_balanced_combine_d<128>(L, stream);
+  if (L.D == 64) return launch_balanced_combine_d<64>(L, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream) {
   if (L.D == 128) return L.sparse ? launch_partial_d<128, true>(L, stream)

@@ -22,9 +22,12 @@ struct PartialLaunch {
   int max_pages;             // block-table row length
   int64_t num_pages;
   uint16_t* out;       // [B, Hq, 1, D] bf16: written directly when S == 1
-  float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1)
-  float* part_m;       // [B*Hq, S] running max, base 2 (S > 1)
-  float* part_l;       // [B*Hq, S] softmax denominators (S > 1)
+  float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1); balanced
+                       // schedule: [balanced_wgs, 2, heads_per_wg, D]
+  float* part_m;       // [B*Hq, S] running max, base 2 (S > 1); balanced: [balanced_wgs, 2,
+                       // heads_per_wg]
+  float* part_l;       // [B*Hq, S] softmax denominators (S > 1); balanced: as part_m
+  int balanced_wgs;    // workgroups of the length-balanced schedule (ragged calls)
   int B, Hq, Hkv, G, D;
   int kv_batch;        // sparse: 1 or B; dense: B
   int64_t capacity;
@@ -39,5 +42,9 @@ struct PartialLaunch {
 
 hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream);
 hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream);
+// Length-balanced pass over per-sequence device lengths (k_len_dev), and the
+// merge of the partials it leaves.
+hipError_t launch_balanced(const PartialLaunch& L, hipStream_t stream);
+hipError_t launch_balanced_combine(const PartialLaunch& L, hipStream_t stream);
 
 }  // namespace da

@@ -85,6 +85,8 @@ typedef struct {
   int32_t max_pages_per_seq; /* paged: block-table row length; capacity must equal
                                 page_size * max_pages_per_seq                            */
   int64_t num_pages;    /* paged: pages in the K and V page pools                         */
+  int32_t ragged;       /* 1: the plan also serves decode_attn_dense_ragged (one length per
+                           sequence; implied by page_size > 0), 0: it does not             */
 } decode_attn_problem;
 
 /*
@@ -99,7 +101,8 @@ typedef struct {
                                dense: keys per split at max_k_len                      */
   int32_t num_cus;          /* compute units the plan was made for                      */
   int32_t kind;             /* 0 dense, 1 sparse                                       */
-  int32_t reserved0;
+  int32_t balanced_wgs;     /* ragged / paged plans: workgroups of the length-balanced
+                               schedule (0 for other plans)                              */
   uint64_t workspace_bytes; /* bytes of workspace every call of this plan needs (may be 0) */
 } decode_attn_plan_t;
 

@@ -58,7 +58,7 @@ RAGGED_SHAPES = [
 @pytest.mark.parametrize("B,Hq,Hkv,D,cap,lens", RAGGED_SHAPES)
 def test_ragged_matches_oracle(da, B, Hq, Hkv, D, cap, lens):
     q, k, v = W.random_case(80 + B, B, Hq, Hkv, D, cap)
-    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap)
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
     out = _out(B, Hq, D)
     H.log(f"ragged B={B} Hq={Hq} Hkv={Hkv} D={D} cap={cap} S={plan.num_splits_max} lens={lens}")
     da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.09,
@@ -75,7 +75,7 @@ def test_ragged_reads_strided_triples(da):
     lens = [2500, 77, 1200, 0]
     q, k, v = W.random_case(90, B, Hq, Hkv, D, cap)
     triples = np.array([[n, 12345, -999] for n in lens], dtype=np.int32)
-    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap)
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
     out = _out(B, Hq, D)
     H.log("ragged stride-3 triples")
     da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.09,
@@ -86,24 +86,46 @@ def test_ragged_reads_strided_triples(da):
     _check_ragged(H.from_dev(out), q, k, v, 0.09, lens, "stride 3")
 
 
-def test_ragged_with_equal_lengths_is_the_devlen_call(da):
-    # every sequence at one length: bit-identical to the single device length
+def test_ragged_schedule_edges(da):
+    # lengths that put run boundaries at stream starts, inside streams and on
+    # sequences shorter than a run; one long sequence cut into many runs; all
+    # sequences empty; a single sequence
     import torch
-    B, Hq, Hkv, D, cap = 4, 32, 8, 128, 6000
+    B, Hq, Hkv, D, cap = 9, 32, 8, 128, 6000
     q, k, v = W.random_case(91, B, Hq, Hkv, D, cap)
-    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap)
     dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
-    ws = da.workspace_for(plan)
-    for n in (1, 4500, 6000):
-        a, b = _out(B, Hq, D), _out(B, Hq, D)
-        H.log(f"ragged == devlen at {n}")
-        da.decode_attn_dense_ragged(plan, dq, dk, dv, a, 0.09,
-                                    torch.full((B,), n, dtype=torch.int32, device="cuda"),
-                                    workspace=ws)
-        da.decode_attn_dense_devlen(plan, dq, dk, dv, b, 0.09,
-                                    torch.full((1,), n, dtype=torch.int32, device="cuda"), ws)
+    for num_cus, lens in ((256, [6000, 1, 32, 33, 0, 4500, 64, 0, 2]),
+                          (4, [6000, 1, 32, 33, 0, 4500, 64, 0, 2]),
+                          (1, [256] * 9),
+                          (256, [0] * 9),
+                          (3, [0, 0, 0, 0, 5999, 0, 0, 0, 0])):
+        plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True, num_cus=num_cus)
+        out = _out(B, Hq, D)
+        H.log(f"ragged schedule cus={num_cus} wgs={plan.balanced_wgs} lens={lens}")
+        da.decode_attn_dense_ragged(plan, dq, dk, dv, out, 0.09, H.to_dev_i32(lens),
+                                    workspace=da.workspace_for(plan))
         torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+        _check_ragged(H.from_dev(out), q, k, v, 0.09, lens, f"cus={num_cus} {lens}")
+
+
+def test_ragged_is_deterministic_and_ignores_workspace_contents(da):
+    import torch
+    B, Hq, Hkv, D, cap = 6, 64, 4, 128, 3000
+    q, k, v = W.random_case(92, B, Hq, Hkv, D, cap)
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True, num_cus=16)
+    dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+    lens = H.to_dev_i32([3000, 17, 2999, 640, 1, 1500])
+    ws = da.workspace_for(plan)
+    outs = []
+    for fill in (0.0, float("nan"), 1e30):
+        ws.view(torch.float32).fill_(fill)
+        out = _out(B, Hq, D)
+        H.log(f"ragged determinism, workspace filled with {fill}")
+        da.decode_attn_dense_ragged(plan, dq, dk, dv, out, 0.09, lens, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert all(torch.equal(outs[0].view(torch.int16), o.view(torch.int16)) for o in outs[1:])
+    _check_ragged(H.from_dev(outs[0]), q, k, v, 0.09, [3000, 17, 2999, 640, 1, 1500], "G=16")
 
 
 PAGED_SHAPES = [
@@ -168,10 +190,10 @@ def test_paged_with_identity_table_is_the_ragged_call(da):
         .reshape(B * max_pages, Hkv, page, D))
     table = np.arange(B * max_pages, dtype=np.int32).reshape(B, max_pages)
     lens = [cap, 1234, 64]
-    ragged = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap)
+    ragged = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
     paged = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, page_size=page,
                                 max_pages_per_seq=max_pages, num_pages=B * max_pages)
-    assert ragged.num_splits_max == paged.num_splits_max
+    assert ragged.balanced_wgs == paged.balanced_wgs
     a, b = _out(B, Hq, D), _out(B, Hq, D)
     H.log("paged identity table == ragged")
     dl = H.to_dev_i32(lens)
@@ -255,7 +277,7 @@ def test_full_size_sampled(da, name):
                                    num_pages=kp.shape[0])
     else:
         q, k, v, lens = W.ragged_inputs(case)
-        plan = da.decode_attn_plan(case.B, case.Hq, case.Hkv, case.D, cap, cap)
+        plan = da.decode_attn_plan(case.B, case.Hq, case.Hkv, case.D, cap, cap, ragged=True)
     out = _out(case.B, case.Hq, case.D)
     H.log(f"full size {name} S={plan.num_splits_max}")
     ws = da.workspace_for(plan)

@@ -239,11 +239,29 @@ def test_paged_plans(da):
         assert ei.value.status == status, kw
 
 
+def test_ragged_plans(da):
+    # the length-balanced schedule: two resident workgroups per CU, two partial
+    # slots of heads_per_wg rows each
+    dense = plan(da)
+    R = plan(da, ragged=True)
+    assert dense.balanced_wgs == 0 and R.balanced_wgs == 512 and R.prob.ragged == 1
+    assert (R.num_splits_max, R.chunk) == (dense.num_splits_max, dense.chunk)
+    assert R.workspace_bytes == max(dense.workspace_bytes, 512 * 2 * 8 * 130 * 4)
+    assert paged_plan(da).balanced_wgs == 512  # paged plans are always ragged
+    tiny = da.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256, ragged=True)
+    assert tiny.workspace_bytes == 512 * 2 * 1 * 66 * 4
+    with pytest.raises(da.DecodeAttnError) as ei:
+        da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=64, kv_batch=1, num_cus=256,
+                            ragged=True)
+    assert ei.value.status == 2 and "ragged" in str(ei.value)
+
+
 def test_ragged_and_paged_fail_closed(da):
     lib = da.library()
     fake = ctypes.c_void_p(0x10000)
     ws = ctypes.c_void_p(0x20000)
-    P = plan(da)
+    D = plan(da)
+    P = plan(da, ragged=True)
     G = paged_plan(da)
     rag = lambda pl, lens=fake, stride=1, w=ws: lib.decode_attn_dense_ragged(  # noqa: E731
         ctypes.byref(pl), fake, fake, fake, fake, 0.1, lens, stride, w, pl.workspace_bytes, None)
@@ -254,6 +272,8 @@ def test_ragged_and_paged_fail_closed(da):
     assert rag(P, lens=ctypes.c_void_p(0x10002)) == 1
     assert rag(P, stride=0) == 1
     assert rag(P, w=None) == 3
+    assert rag(D) == 1                          # a plan made without ragged = 1
+    assert "ragged" in da.decode_attn_last_error()
     assert rag(G) == 1                          # a paged plan needs the paged call
     assert "paged" in da.decode_attn_last_error()
     assert pag(P) == 1                          # a contiguous plan handed to the paged call
