@@ -8,6 +8,12 @@ The arithmetic lives in ``decode_oracle.c`` (plain C, fp64, the definition of
 softmax attention written out; see the header of that file for the readings it
 takes). This module compiles it with gcc and marshals numpy arrays into it.
 
+The multi-token, ragged and paged forms (``dense_tokens``, ``dense_ragged``,
+``dense_paged``) are compositions of ``dense``: one call per token and
+sequence over the rows that token sees, pages gathered back into rows first.
+They are pinned by ``tests/test_ragged_oracle.py`` and
+``tests/test_tokens_oracle.py``.
+
 Pinned by ``tests/test_oracle.py`` against closed forms and invariants (one
 key returns its value row; identical keys return the mean of V; a zero scale
 returns the mean; two keys follow the logistic closed form; the GQA head map;
@@ -128,16 +134,40 @@ def sparse(q, k, v, sel, scale: float, k_len: int | None = None, rows=None,
     return out.reshape(B, Hq, 1, D) if r is None else out
 
 
-def dense_ragged(q, k, v, scale: float, k_lens, threads: int | None = None):
-    """Dense attention where sequence b attends rows [0, k_lens[b]) of its own
-    cache (a length of 0 gives zeros). The dense oracle, one sequence at a time."""
+def visible_keys(k_len: int, seq_q: int, t: int, causal: bool) -> int:
+    """Keys visible to query token t of seq_q when the live prefix k_len already
+    counts the seq_q new tokens (DecodeFlashSpec, field k_len: cached length plus
+    the new tokens). Causal: token t sits at position k_len - seq_q + t and sees
+    rows [0, k_len - seq_q + t + 1); otherwise every token sees [0, k_len)."""
+    return max(0, k_len - (seq_q - 1 - t)) if causal else max(0, k_len)
+
+
+def dense_tokens(q, k, v, scale: float, k_len: int, causal: bool = True,
+                 threads: int | None = None):
+    """q [B,Hq,Sq,D] against k/v [B,Hkv,capacity,D]: token t attends rows
+    [0, visible_keys(k_len, Sq, t, causal)); an empty prefix gives zeros. The
+    single-token oracle, one token at a time."""
     q = _bits(q, 4)
-    B, Hq, _, D = q.shape
-    out = np.zeros((B, Hq, 1, D), dtype=np.float64)
-    for b in range(B):
-        n = int(k_lens[b])
+    B, Hq, Sq, D = q.shape
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    for t in range(Sq):
+        n = visible_keys(int(k_len), Sq, t, causal)
         if n > 0:
-            out[b] = dense(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale, n, threads=threads)[0]
+            out[:, :, t:t + 1] = dense(q[:, :, t:t + 1], k, v, scale, n, threads=threads)
+    return out
+
+
+def dense_ragged(q, k, v, scale: float, k_lens, causal: bool = True,
+                 threads: int | None = None):
+    """Dense attention where sequence b attends rows [0, k_lens[b]) of its own
+    cache (a length of 0 gives zeros; with several query tokens, token t sees
+    visible_keys of them). The token oracle, one sequence at a time."""
+    q = _bits(q, 4)
+    B, Hq, Sq, D = q.shape
+    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    for b in range(B):
+        out[b] = dense_tokens(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale, int(k_lens[b]), causal,
+                              threads=threads)[0]
     return out
 
 
@@ -160,7 +190,7 @@ def unpage(pages, block_table, n_rows: int):
     return out
 
 
-def dense_paged(q, k_pages, v_pages, block_table, scale: float, k_lens,
+def dense_paged(q, k_pages, v_pages, block_table, scale: float, k_lens, causal: bool = True,
                 threads: int | None = None):
     """Attention over a paged cache: the pages gathered into contiguous rows,
     then the ragged dense oracle."""
@@ -168,4 +198,4 @@ def dense_paged(q, k_pages, v_pages, block_table, scale: float, k_lens,
     n_rows = block_table.shape[1] * page_size
     k = unpage(k_pages, block_table, n_rows)
     v = unpage(v_pages, block_table, n_rows)
-    return dense_ragged(q, k, v, scale, k_lens, threads=threads)
+    return dense_ragged(q, k, v, scale, k_lens, causal, threads=threads)
