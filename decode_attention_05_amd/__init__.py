@@ -226,9 +226,10 @@ def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int
     import torch
     p = plan.prob
     B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    Sq = p.seq_q
     bf = torch.bfloat16
-    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
-            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    args = (_tensor_ptr(q, "q", (B, Hq, Sq, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense(ctypes.byref(plan), *args, float(softmax_scale), int(k_len),
                                        ws, wsb, _stream_ptr(stream)))
@@ -242,9 +243,10 @@ def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_l
     import torch
     p = plan.prob
     B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    Sq = p.seq_q
     bf = torch.bfloat16
-    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
-            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    args = (_tensor_ptr(q, "q", (B, Hq, Sq, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     klen = _tensor_ptr(k_len_dev, "k_len_dev", (1,), torch.int32)
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense_devlen(ctypes.byref(plan), *args, float(softmax_scale),
@@ -268,9 +270,10 @@ def decode_attn_dense_ragged(plan: Plan, q, k, v, out, softmax_scale: float, k_l
     import torch
     p = plan.prob
     B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    Sq = p.seq_q
     bf = torch.bfloat16
-    args = (_tensor_ptr(q, "q", (B, Hq, 1, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
-            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, 1, D), bf))
+    args = (_tensor_ptr(q, "q", (B, Hq, Sq, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     lens = _lens_ptr(k_lens, B, k_lens_stride)
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense_ragged(ctypes.byref(plan), *args, float(softmax_scale),
@@ -286,15 +289,15 @@ def decode_attn_dense_paged(plan: Plan, q, k_pages, v_pages, block_table, k_lens
     block_table [B, max_pages_per_seq] (int32, device)."""
     import torch
     p = plan.prob
-    B, Hq, Hkv, D = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim
+    B, Hq, Hkv, D, Sq = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.seq_q
     bf = torch.bfloat16
     pool = (p.num_pages, Hkv, p.page_size, D)
-    qp = _tensor_ptr(q, "q", (B, Hq, 1, D), bf)
+    qp = _tensor_ptr(q, "q", (B, Hq, Sq, D), bf)
     kp = _tensor_ptr(k_pages, "k_pages", pool, bf)
     vp = _tensor_ptr(v_pages, "v_pages", pool, bf)
     bt = _tensor_ptr(block_table, "block_table", (B, p.max_pages_per_seq), torch.int32)
     lens = _lens_ptr(k_lens, B, k_lens_stride)
-    op = _tensor_ptr(out, "out", (B, Hq, 1, D), bf)
+    op = _tensor_ptr(out, "out", (B, Hq, Sq, D), bf)
     ws, wsb = _ws_ptr(plan, workspace)
     _check(library().decode_attn_dense_paged(ctypes.byref(plan), qp, kp, vp, bt, lens,
                                              int(k_lens_stride), op, float(softmax_scale), ws, wsb,

@@ -3,8 +3,10 @@
 // live in kernels.hip.
 //
 // The problem statement follows the fuel-dispatch page "DecodeFlashSpec"
-// (shapes of q, k, v; softmax_scale; k_len as the live prefix; causal accepted
-// and ignored; ALiBi, windows and softcap rejected); the sparse call follows
+// (shapes of q, k, v; softmax_scale; k_len as the live prefix, counting the
+// query tokens of the pass; causal accepted and ignored for one token, applied
+// to the last Sq positions of the prefix for several; ALiBi, windows and
+// softcap rejected); the sparse call follows
 // the metrale page "AttnV41" (decode_fixed_topk: a fixed launch width padded
 // with -1). Validation fails closed on host-visible values only, and no call
 // synchronises or copies, as the flashinfer page "packed_fused_kda_decode"
@@ -101,17 +103,21 @@ int64_t splits_for_occupancy(int64_t units, int cus) {
   return std::max<int64_t>(1, (int64_t)kResidentPerCu * cus / units);
 }
 
-int heads_per_wg(int G) {
-  for (int gt = 16; gt > 1; --gt)
+// Query heads per workgroup: the largest divisor of G whose rows (heads times
+// tokens) fit the 16 columns of one MFMA tile.
+int heads_per_wg(int G, int Sq) {
+  for (int gt = 16 / Sq; gt > 1; --gt)
     if (G % gt == 0) return gt;
   return 1;
 }
+
+constexpr int kMaxSeqQ = 16;
 
 // Number of splits and keys per split for one dense call of length k_len.
 void dense_split(const decode_attn_plan_t& P, int64_t k_len, int* S_out, int* chunk_out,
                  int* bound_out) {
   const auto& p = P.prob;
-  const int gt = heads_per_wg(P.group);
+  const int gt = heads_per_wg(P.group, p.seq_q);
   const int64_t units = (int64_t)p.batch * p.num_kv_heads * (P.group / gt);
   int64_t chunk, S, bound;
   if (p.force_chunk > 0) {
@@ -139,9 +145,11 @@ decode_attn_status validate_problem(const decode_attn_problem& p) {
   if (p.window_right != -1)
     return fail(DA_ERR_UNSUPPORTED, "window_right: sliding windows are not supported");
   if (p.has_softcap) return fail(DA_ERR_UNSUPPORTED, "softcap: logit softcap is not supported");
-  if (p.seq_q != 1)
-    return fail(DA_ERR_UNSUPPORTED, "seq_q: only single-token decode (seq_q == 1) is supported, got %d",
-                p.seq_q);
+  if (p.seq_q < 1 || p.seq_q > kMaxSeqQ)
+    return fail(DA_ERR_UNSUPPORTED, "seq_q: 1 to %d query tokens per sequence are supported, got %d",
+                kMaxSeqQ, p.seq_q);
+  if (p.seq_q > 1 && p.topk_max > 0)
+    return fail(DA_ERR_UNSUPPORTED, "seq_q: the sparse call takes one query token per sequence");
   if (p.head_dim != 64 && p.head_dim != 128)
     return fail(DA_ERR_UNSUPPORTED, "head_dim: only 64 and 128 are supported, got %d", p.head_dim);
   if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1)
@@ -187,7 +195,7 @@ decode_attn_status validate_problem(const decode_attn_problem& p) {
   // Element counts must fit the 64-bit index arithmetic with ample margin.
   const double elems = (double)p.batch * p.num_kv_heads * (double)p.capacity * p.head_dim;
   if (elems > 9.0e15) return fail(DA_ERR_INVALID_ARG, "KV buffer too large");
-  if ((int64_t)p.batch * p.num_q_heads > 0x7fffffff)
+  if ((int64_t)p.batch * p.num_q_heads * p.seq_q > 0x7fffffff)
     return fail(DA_ERR_INVALID_ARG, "batch * num_q_heads too large");
   return DA_OK;
 }
@@ -212,9 +220,11 @@ da::PartialLaunch base_launch(const decode_attn_plan_t& P, const void* q, const 
   L.capacity = p.capacity;
   L.k_len = k_len;
   L.S = S;
-  L.heads_per_wg = heads_per_wg(P.group);
+  L.heads_per_wg = heads_per_wg(P.group, p.seq_q);
+  L.Sq = p.seq_q;
+  L.causal = p.causal != 0;
   L.qscale = scale * 1.4426950408889634f;  // log2(e): the kernels use exp2
-  const int64_t rows = (int64_t)p.batch * p.num_q_heads;
+  const int64_t rows = (int64_t)p.batch * p.num_q_heads * p.seq_q;
   float* ws = static_cast<float*>(workspace);
   L.part_o = S > 1 ? ws : nullptr;
   L.part_m = S > 1 ? ws + rows * S * p.head_dim : nullptr;
@@ -224,13 +234,15 @@ da::PartialLaunch base_launch(const decode_attn_plan_t& P, const void* q, const 
 
 uint64_t workspace_for(const decode_attn_problem& p, int S) {
   if (S <= 1) return 0;
-  return (uint64_t)p.batch * p.num_q_heads * (uint64_t)S * (p.head_dim + 2) * sizeof(float);
+  return (uint64_t)p.batch * p.num_q_heads * p.seq_q * (uint64_t)S * (p.head_dim + 2) *
+         sizeof(float);
 }
 
-// Length-balanced schedule: two partial slots of heads_per_wg rows per workgroup.
+// Length-balanced schedule: two partial slots of (heads per workgroup) x
+// (tokens) rows per workgroup.
 uint64_t balanced_workspace(const decode_attn_plan_t& P) {
-  return (uint64_t)P.balanced_wgs * 2 * heads_per_wg(P.group) * (P.prob.head_dim + 2) *
-         sizeof(float);
+  return (uint64_t)P.balanced_wgs * 2 * heads_per_wg(P.group, P.prob.seq_q) * P.prob.seq_q *
+         (P.prob.head_dim + 2) * sizeof(float);
 }
 
 decode_attn_status check_common(const decode_attn_plan_t* plan, int kind, const void* q,
@@ -301,7 +313,7 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
   L.k_lens_stride = k_lens_stride;
   L.sparse = false;
   L.balanced_wgs = plan->balanced_wgs;
-  const int64_t slots = (int64_t)plan->balanced_wgs * 2 * L.heads_per_wg;
+  const int64_t slots = (int64_t)plan->balanced_wgs * 2 * L.heads_per_wg * L.Sq;
   float* ws = static_cast<float*>(workspace);
   L.part_o = ws;
   L.part_m = ws + slots * plan->prob.head_dim;
@@ -351,7 +363,7 @@ decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_pl
     if (s != DA_OK) return s;
   }
   P.num_cus = cus;
-  const int gt = heads_per_wg(P.group);
+  const int gt = heads_per_wg(P.group, p->seq_q);
   const int64_t units = (int64_t)p->batch * p->num_kv_heads * (P.group / gt);
   if (P.kind == 0) {
     int S = 0, chunk = 0, bound = 0;
@@ -403,6 +415,10 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
   if (k_len < 1 || k_len > plan->prob.max_k_len)
     return fail(DA_ERR_INVALID_ARG, "k_len must lie in [1, max_k_len = %lld], got %lld",
                 (long long)plan->prob.max_k_len, (long long)k_len);
+  if (plan->prob.causal && k_len < plan->prob.seq_q)
+    return fail(DA_ERR_INVALID_ARG,
+                "k_len (%lld) counts the %d query tokens and must be at least that many",
+                (long long)k_len, plan->prob.seq_q);
   int S = 0, chunk = 0;
   dense_split(*plan, k_len, &S, &chunk, nullptr);
   if (S > plan->num_splits_max)

@@ -94,6 +94,7 @@ struct TileRegs {
   uint4 k[2][Geometry<D>::NC];   // A operands: key rows (lane % 16) of the two 16-key halves
   uint4 v[Geometry<D>::VLD];     // V tile in natural order, destined for LDS
   uint32_t mask;                 // bit i: key i of the tile is valid
+  int tau;                       // tile index within the range
 };
 
 // Where attend_range leaves the result of its GT heads: the bf16 output rows
@@ -110,19 +111,21 @@ struct RangeOut {
   int64_t pm_stride;
 };
 
-// The whole workgroup attends the GT query heads h0 .. h0 + GT - 1 of sequence
-// b (kv head hkv) over keys [j0, j1) of its KV stream (dense: rows of the cache;
-// sparse: entries of the selection), k_len bounding the usable rows, and
-// writes the merged result of its four waves to `ro`. Every thread of the
-// workgroup must call it with the same arguments; it synchronises the
-// workgroup and uses all of `lds`, so a caller that calls it again first
-// synchronises.
+// The whole workgroup attends the RT query rows row0 .. row0 + RT - 1 (rows of
+// q [B, Hq, Sq, D] flattened: heads h0 .. h0 + RT / Sq - 1 of sequence b, every
+// token of each) through kv head hkv over keys [j0, j1) of its KV stream
+// (dense: rows of the cache; sparse: entries of the selection), k_len bounding
+// the usable rows, and writes the merged result of its four waves to `ro`.
+// With causal masking and several tokens, token t sees only keys below
+// k_len - Sq + 1 + t. Every thread of the workgroup must call it with the same
+// arguments; it synchronises the workgroup and uses all of `lds`, so a caller
+// that calls it again first synchronises.
 template <int D, bool SPARSE>
 __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned char* lds,
                                              float (&mrg_m)[kWaves][16],
-                                             float (&mrg_l)[kWaves][16], int b, int hkv, int h0,
-                                             int GT, int64_t k_len, int64_t j0, int64_t j1,
-                                             const RangeOut& ro) {
+                                             float (&mrg_l)[kWaves][16], int b, int hkv,
+                                             int64_t row0, int RT, int64_t k_len, int64_t j0,
+                                             int64_t j1, const RangeOut& ro) {
   using Gm = Geometry<D>;
   constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
 
@@ -136,12 +139,11 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   const int g = lane >> 4;   // lane group: which 8 bf16 of a 32-wide k slice
   const int r16 = lane & 15; // A-operand row / C-operand column
 
-  // B operand of S^T = K Q^T: lane holds q[h0 + r16][8 (4c + g) .. + 7].
+  // B operand of S^T = K Q^T: lane holds q row row0 + r16, elements 8 (4c + g) .. + 7.
   bf16x8 qop[NC];
   {
-    const bool hv = r16 < GT;
-    const uint4* qrow =
-        reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.Hq + h0 + (hv ? r16 : 0)) * D);
+    const bool hv = r16 < RT;
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + (row0 + (hv ? r16 : 0)) * D);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       qop[c] = as_bf16x8(hv ? qrow[4 * c + g] : make_uint4(0u, 0u, 0u, 0u));
@@ -153,6 +155,18 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   const uint4* __restrict__ vp = reinterpret_cast<const uint4*>(a.v + kv_base);
 
   const int ntiles = (j1 > j0) ? (int)((j1 - j0 + kTileKeys - 1) / kTileKeys) : 0;
+  // Causal masking of several tokens: keys from k_len - (Sq - 1) on are
+  // visible to some rows only; row r16 (token t = r16 % Sq) sees keys below
+  // k_len - (Sq - 1 - t). Offsets relative to j0 (a range spans < 2^31 keys):
+  // tiles from tail_tau on need per-row masks; lim_rel is k_len - j0.
+  int tail_tau = 0x7fffffff;
+  int lim_rel = 0;
+  if (!SPARSE && a.causal && a.Sq > 1) {
+    const int64_t t0 = k_len - (a.Sq - 1) - j0;  // first key seen by some rows only
+    tail_tau = t0 <= 0 ? 0 : (int)(t0 / kTileKeys);  // tile tau ends at 32 (tau + 1)
+    lim_rel = (int)(k_len - j0);
+  }
+  const int row_off = a.Sq - 1 - r16 % a.Sq;
   const int32_t* sel_row = SPARSE ? a.sel + (int64_t)b * a.topk : nullptr;
 
   unsigned char* vt = lds + wave * Gm::VTILE;  // this wave's V tile
@@ -166,6 +180,7 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vp);
   auto load_tile = [&](TileRegs<D>& R, int tau) {
     const int64_t kt = j0 + (int64_t)tau * kTileKeys;
+    R.tau = tau;
     const unsigned char* kb;
     const unsigned char* vb;
     int row_lane = 0;  // sparse: row of key (lane & 31) of the tile (0 for a pad)
@@ -260,25 +275,33 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[0][c]), qop[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[1][c]), qop[c], s1, 0, 0, 0);
     }
+    uint32_t lm = mask;  // keys this lane's row may see
+    if (R.tau >= tail_tau) {
+      const int rel = lim_rel - kTileKeys * R.tau - row_off;  // keys of this tile it sees
+      lm &= rel >= 32 ? 0xffffffffu : (rel <= 0 ? 0u : ((1u << rel) - 1u));
+    }
     float sc[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
-      sc[i] = ((mask >> k0) & 1u) ? s0[i] * qscale : kNegInf;
-      sc[4 + i] = ((mask >> k1) & 1u) ? s1[i] * qscale : kNegInf;
+      sc[i] = ((lm >> k0) & 1u) ? s0[i] * qscale : kNegInf;
+      sc[4 + i] = ((lm >> k1) & 1u) ? s1[i] * qscale : kNegInf;
     }
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);  // finite: the tile holds a valid key
-    const float alpha = exp2_fast(m - m_new);
+    const float m_new = fmaxf(m, mx);
+    // -inf only for a row that has seen no key yet (causal rows): then every
+    // weight below is exp2(-inf) = 0 and the state stays empty.
+    const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2_fast(m - m_ref);
     uint32_t pw[4];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pw[i] = pack_bf16(exp2_fast(sc[2 * i] - m_new), exp2_fast(sc[2 * i + 1] - m_new));
+      pw[i] = pack_bf16(exp2_fast(sc[2 * i] - m_ref), exp2_fast(sc[2 * i + 1] - m_ref));
       psum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xffff0000u);
     }
     l = l * alpha + psum;
@@ -342,7 +365,7 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   // Merge the waves in order 0..3. Thread t owns head t / 16 and D/16 values.
   constexpr int PER = D / 16;
   const int hh = tid >> 4, d0 = (tid & 15) * PER;
-  if (hh < GT) {
+  if (hh < RT) {
     float M = kNegInf, L = 0.f, acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   const int64_t j_end = SPARSE ? (int64_t)a.topk : k_len;
   const int64_t j1 = (j0 + chunk < j_end) ? j0 + chunk : j_end;
 
-  const int64_t row0 = (int64_t)b * a.Hq + h0;
+  const int64_t row0 = ((int64_t)b * a.Hq + h0) * a.Sq;
   RangeOut ro;
   ro.direct = a.S == 1;
   ro.out = a.out + row0 * D;
@@ -437,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
   ro.pl = a.S > 1 ? a.part_l + row0 * a.S + s : nullptr;
   ro.po_stride = (int64_t)a.S * D;
   ro.pm_stride = a.S;
-  attend_range<D, SPARSE>(a, lds, mrg_m, mrg_l, b, hkv, h0, GT, k_len, j0, j1, ro);
+  attend_range<D, SPARSE>(a, lds, mrg_m, mrg_l, b, hkv, row0, GT * a.Sq, k_len, j0, j1, ro);
 }
 
 // --- length-balanced schedule (one live length per sequence) ----------------
@@ -504,6 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
 
   const int lane = threadIdx.x & 63;
   const int GT = a.heads_per_wg;
+  const int RT = GT * a.Sq;             // query rows of one stream
   const int tiles_h = a.G / GT;
   const int per_seq = a.Hkv * tiles_h;  // streams per sequence
   const Schedule sc = balanced_schedule(a, per_seq);
@@ -550,18 +574,18 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
     const int64_t left = t1 - x;
     const int64_t nt = (nb - jt < left) ? nb - jt : left;
     const int hkv = r / tiles_h, ht = r % tiles_h;
-    const int h0 = hkv * a.G + ht * GT;
+    const int64_t row0 = ((int64_t)b * a.Hq + hkv * a.G + ht * GT) * a.Sq;
     RangeOut ro;
     ro.direct = (jt == 0 && nt == nb);  // the whole stream is in this run
-    ro.out = a.out + ((int64_t)b * a.Hq + h0) * D;
-    const int64_t slot = ((int64_t)blockIdx.x * 2 + (x == t0 ? 0 : 1)) * GT;
+    ro.out = a.out + row0 * D;
+    const int64_t slot = ((int64_t)blockIdx.x * 2 + (x == t0 ? 0 : 1)) * RT;
     ro.po = a.part_o + slot * D;
     ro.pm = a.part_m + slot;
     ro.pl = a.part_l + slot;
     ro.po_stride = D;
     ro.pm_stride = 1;
     const int64_t j1 = (jt + nt) * kTileKeys;
-    attend_range<D, false>(a, lds, mrg_m, mrg_l, b, hkv, h0, GT, len, jt * kTileKeys,
+    attend_range<D, false>(a, lds, mrg_m, mrg_l, b, hkv, row0, RT, len, jt * kTileKeys,
                            j1 < len ? j1 : len, ro);
     x += nt;
     if (x >= t1) break;
@@ -594,10 +618,11 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
   const int GT = a.heads_per_wg;
   const int tiles_h = a.G / GT;
   const int per_seq = a.Hkv * tiles_h;
+  const int RT = GT * a.Sq;
   const int b = blockIdx.x / per_seq, r = blockIdx.x % per_seq;
   const int h0 = (r / tiles_h) * a.G + (r % tiles_h) * GT;
-  const int hh = tid >> 4, t16 = tid & 15, d0 = t16 * PER;
-  uint16_t* out = a.out + ((int64_t)b * a.Hq + h0 + hh) * D + d0;
+  const int hh = tid >> 4, t16 = tid & 15, d0 = t16 * PER;  // row hh of the stream
+  uint16_t* out = a.out + (((int64_t)b * a.Hq + h0) * a.Sq + hh) * D + d0;
 
   // One pass over the lengths: all tiles (the schedule) and the tiles before b.
   int64_t all = 0, before = 0;
@@ -612,7 +637,7 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
   const int64_t per_wg = even > kMinTilesPerWg ? even : kMinTilesPerWg;
   const int64_t nb = tiles_of(seq_len(a, b));
   if (nb == 0) {
-    if (hh < GT) {
+    if (hh < RT) {
       if constexpr (PER == 8)
         *reinterpret_cast<uint4*>(out) = make_uint4(0u, 0u, 0u, 0u);
       else
@@ -622,11 +647,11 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
   }
   const int64_t ts = uniform_i64(wave_sum_i64(before)) * per_seq + (int64_t)r * nb;
   const int64_t ws = ts / per_wg, we = (ts + nb - 1) / per_wg;
-  if (ws == we || hh >= GT) return;
+  if (ws == we || hh >= RT) return;
 
   auto slot_of = [&](int64_t w) -> int64_t {
     const int first = (w > ws || ts == w * per_wg) ? 0 : 1;
-    return (w * 2 + first) * GT + hh;
+    return (w * 2 + first) * RT + hh;
   };
   // M over the pieces: the 16 threads of a head take every 16th piece.
   float M = kNegInf;
@@ -730,7 +755,8 @@ template <int D, bool SPARSE>
 hipError_t launch_partial_d(const PartialLaunch& L, hipStream_t stream) {
   const int tiles = L.G / L.heads_per_wg;
   const int64_t grid = (int64_t)L.B * L.Hkv * tiles * L.S;
-  if (grid <= 0 || grid > 0x7fffffff || L.heads_per_wg < 1 || L.heads_per_wg > 16)
+  if (grid <= 0 || grid > 0x7fffffff || L.heads_per_wg < 1 || L.heads_per_wg * L.Sq > 16 ||
+      (SPARSE && L.Sq != 1))
     return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attend_partial<D, SPARSE>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      L);
@@ -753,8 +779,8 @@ hipError_t launch_balanced_combine_d(const PartialLaunch& L, hipStream_t stream)
 
 bool balanced_ok(const PartialLaunch& L) {
   const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
-  return !L.sparse && L.k_len_dev && L.balanced_wgs > 0 && L.heads_per_wg >= 1 &&
-         L.heads_per_wg <= 16 && streams > 0 && streams <= 0x7fffffff && L.part_o && L.part_m &&
+  return !L.sparse && L.k_len_dev && L.balanced_wgs > 0 && L.heads_per_wg >= 1 && L.Sq >= 1 &&
+         L.heads_per_wg * L.Sq <= 16 && streams > 0 && streams <= 0x7fffffff && L.part_o && L.part_m &&
          L.part_l;
 }
 
@@ -783,7 +809,7 @@ hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream) {
-  const int64_t rows = (int64_t)L.B * L.Hq;
+  const int64_t rows = (int64_t)L.B * L.Hq * L.Sq;
   if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (L.D == 128)
     hipLaunchKernelGGL(combine_splits<128>, dim3((unsigned)rows), dim3(256), 0, stream, L);

@@ -8,7 +8,7 @@ namespace da {
 
 // Everything one split-K pass needs. Pointers are device pointers.
 struct PartialLaunch {
-  const uint16_t* q;   // [B, Hq, 1, D] bf16
+  const uint16_t* q;   // [B, Hq, Sq, D] bf16
   const uint16_t* k;   // [kv_batch, Hkv, capacity, D] bf16
   const uint16_t* v;
   const int32_t* sel;  // sparse only: [B, topk]
@@ -21,12 +21,12 @@ struct PartialLaunch {
   int page_size;             // rows per page, a multiple of the 32-key tile
   int max_pages;             // block-table row length
   int64_t num_pages;
-  uint16_t* out;       // [B, Hq, 1, D] bf16: written directly when S == 1
-  float* part_o;       // [B*Hq, S, D] fp32 unnormalised partial outputs (S > 1); balanced
+  uint16_t* out;       // [B, Hq, Sq, D] bf16: written directly when S == 1
+  float* part_o;       // [B*Hq*Sq, S, D] fp32 unnormalised partial outputs (S > 1); balanced
                        // schedule: [balanced_wgs, 2, heads_per_wg, D]
-  float* part_m;       // [B*Hq, S] running max, base 2 (S > 1); balanced: [balanced_wgs, 2,
+  float* part_m;       // [B*Hq*Sq, S] running max, base 2 (S > 1); balanced: [balanced_wgs, 2,
                        // heads_per_wg]
-  float* part_l;       // [B*Hq, S] softmax denominators (S > 1); balanced: as part_m
+  float* part_l;       // [B*Hq*Sq, S] softmax denominators (S > 1); balanced: as part_m
   int balanced_wgs;    // workgroups of the length-balanced schedule (ragged calls)
   int B, Hq, Hkv, G, D;
   int kv_batch;        // sparse: 1 or B; dense: B
@@ -36,6 +36,9 @@ struct PartialLaunch {
   int chunk;           // keys (dense) or selection entries (sparse) per split
   int S;               // number of splits
   int heads_per_wg;    // query heads of one group handled by one workgroup
+  int Sq;              // query tokens per sequence: q and out are [B, Hq, Sq, D]; dense
+                       // only above 1, heads_per_wg * Sq <= 16
+  bool causal;         // Sq > 1: token t sees keys below k_len - Sq + 1 + t
   float qscale;        // softmax_scale * log2(e)
   bool sparse;
 };

@@ -1,17 +1,19 @@
 /*
- * decode_attn.h -- single-token decode attention on MI355X (gfx950), C ABI.
+ * decode_attn.h -- decode attention on MI355X (gfx950), C ABI.
  *
- * The operation. For one query token per sequence,
+ * The operation. For query token t of Sq (Sq = 1 in plain decode),
  *
- *     out[b, h, 0, :] = sum_j softmax_j( softmax_scale * q[b, h, 0, :] . K[b, hk, j, :] ) V[b, hk, j, :]
+ *     out[b, h, t, :] = sum_j softmax_j( softmax_scale * q[b, h, t, :] . K[b, hk, j, :] ) V[b, hk, j, :]
  *
- * with hk = h / (Hq / Hkv) (grouped-query heads: each KV head serves a
- * contiguous group of Hq / Hkv query heads). This is the problem stated by the
- * fuel-dispatch page "DecodeFlashSpec": q is [B, Hq, Sq, D]; k and v are the
- * capacity KV buffers [B, Hkv, capacity, D]; softmax_scale is an f32 (usually
- * 1/sqrt(head_dim)); the query attends the live prefix [0, k_len) (field
- * k_len); causal is accepted and ignored since a single query row sees the
- * whole prefix (field causal); ALiBi slopes, left and right sliding windows
+ * over the keys j the token sees, with hk = h / (Hq / Hkv) (grouped-query
+ * heads: each KV head serves a contiguous group of Hq / Hkv query heads). This
+ * is the problem stated by the fuel-dispatch page "DecodeFlashSpec": q is
+ * [B, Hq, Sq, D]; k and v are the capacity KV buffers [B, Hkv, capacity, D];
+ * softmax_scale is an f32 (usually 1/sqrt(head_dim)); the query attends the
+ * live prefix [0, k_len), which counts the Sq new tokens (field k_len); causal
+ * is accepted and ignored for one token, which sees the whole prefix (field
+ * causal), and for several tokens masks each to the positions up to its own
+ * (the last Sq of the prefix); ALiBi slopes, left and right sliding windows
  * and a logit softcap are rejected (fields alibi, window_size_left,
  * window_size_right, softcap).
  *
@@ -63,17 +65,22 @@ typedef enum {
  * decode_fixed_topk).
  */
 typedef struct {
-  int32_t batch;        /* B >= 1: query tokens (one per sequence)                        */
+  int32_t batch;        /* B >= 1: sequences                                              */
   int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads                            */
   int32_t num_kv_heads; /* Hkv >= 1                                                       */
   int32_t head_dim;     /* D: 64 or 128                                                   */
-  int32_t seq_q;        /* Sq: must be 1 (single-token decode)                            */
+  int32_t seq_q;        /* Sq: query tokens per sequence, 1 (decode) to 16 (verification
+                           rows: the AttnV41 page's forward runs m tokens at start_pos);
+                           above 1 for dense plans only                                 */
   int64_t capacity;     /* rows per (kv batch, kv head) in K and V                        */
   int64_t max_k_len;    /* largest k_len a call may pass, 1 <= max_k_len <= capacity      */
   int32_t topk_max;     /* sparse plan: largest launch topk (>= 1); 0 = dense plan        */
   int32_t kv_batch;     /* sparse: 1 (rows shared by all tokens) or batch; dense: batch
                            (0 is read as batch)                                           */
-  int32_t causal;       /* accepted and ignored                                           */
+  int32_t causal;       /* Sq = 1: accepted and ignored. Sq > 1: nonzero -> token t (of
+                           Sq) sees rows [0, k_len - Sq + 1 + t), the new tokens being the
+                           last Sq positions of the live prefix; 0 -> every token sees
+                           [0, k_len)                                                    */
   int32_t has_alibi;    /* nonzero -> DA_ERR_UNSUPPORTED                                  */
   int64_t window_left;  /* -1 = none; any other value -> DA_ERR_UNSUPPORTED               */
   int64_t window_right; /* -1 = none; any other value -> DA_ERR_UNSUPPORTED               */
@@ -110,16 +117,19 @@ typedef struct {
  * Validate a problem and choose the split-K decomposition.
  *   p    host pointer to the problem; out  host pointer that receives the plan.
  * Returns DA_OK, DA_ERR_INVALID_ARG (shapes/ranges), DA_ERR_UNSUPPORTED (ALiBi,
- * window, softcap, head_dim other than 64/128, seq_q != 1), or DA_ERR_HIP when
+ * window, softcap, head_dim other than 64/128, seq_q outside 1..16 or above 1 in
+ * a sparse plan, ragged or paged sparse plans), or DA_ERR_HIP when
  * num_cus is 0 and the device query fails. Touches the GPU only for that query.
  */
 decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_plan_t* out);
 
 /*
  * Dense decode attention over the live prefix [0, k_len) of the capacity buffers.
- *   q    [B, Hq, 1, D] bf16            k, v [B, Hkv, capacity, D] bf16
- *   out  [B, Hq, 1, D] bf16 (written)  softmax_scale  finite f32
- *   k_len  1 <= k_len <= plan->prob.max_k_len; rows >= k_len are never read
+ *   q    [B, Hq, Sq, D] bf16           k, v [B, Hkv, capacity, D] bf16
+ *   out  [B, Hq, Sq, D] bf16 (written) softmax_scale  finite f32
+ *   k_len  1 <= k_len <= plan->prob.max_k_len (and k_len >= Sq when causal); rows
+ *          >= k_len are never read. It counts the Sq query tokens (DecodeFlashSpec,
+ *          field k_len: cached length plus the tokens of the pass).
  *   workspace  device scratch of at least plan->workspace_bytes (may be NULL when
  *          that is 0); its contents on entry do not matter.
  * Enqueues one or two kernels on `stream` and returns without waiting.
@@ -157,7 +167,8 @@ decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, cons
  * read straight out of such an array). Same arguments as decode_attn_dense
  * except:
  *   k_lens  device int32; sequence b attends rows [0, k_lens[b * k_lens_stride]).
- *          Values are caller-owned: clamped to [0, max_k_len]; 0 gives zeros.
+ *          Values are caller-owned: clamped to [0, max_k_len]; 0 gives zeros, and
+ *          with causal Sq > 1 a token whose prefix is empty gets zeros.
  *   k_lens_stride  >= 1, in int32 elements (3 for the triples above).
  * The launch is sized once for max_k_len (capturable, like
  * decode_attn_dense_devlen). Returns as decode_attn_dense.

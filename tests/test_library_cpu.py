@@ -80,13 +80,34 @@ def plan(da, **kw):
 
 @pytest.mark.parametrize("field,value", [("has_alibi", True), ("window_left", 128),
                                          ("window_right", 0), ("has_softcap", True),
-                                         ("seq_q", 2), ("head_dim", 96)])
+                                         ("seq_q", 17), ("seq_q", 0), ("head_dim", 96)])
 def test_rejected_features(da, field, value):
     with pytest.raises(da.DecodeAttnError) as ei:
         plan(da, **{field: value})
     assert ei.value.status == 2  # DA_ERR_UNSUPPORTED
     name = field if field not in ("has_alibi", "has_softcap") else field[4:]
     assert name in str(ei.value)
+
+
+def test_several_query_tokens(da):
+    # heads per workgroup shrink so that heads x tokens fit one 16-row tile;
+    # the workspace counts every token's rows; sparse plans take one token
+    one = plan(da, num_cus=256)
+    four = plan(da, seq_q=4, num_cus=256)
+    assert four.prob.seq_q == 4
+    sixteen = plan(da, seq_q=16, ragged=True)
+    assert sixteen.workspace_bytes >= 512 * 2 * 16 * 130 * 4
+    assert four.num_splits_max <= one.num_splits_max
+    with pytest.raises(da.DecodeAttnError) as ei:
+        da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=64, kv_batch=1, num_cus=256, seq_q=2)
+    assert ei.value.status == 2 and "seq_q" in str(ei.value)
+    # a causal static call must cover its own tokens
+    lib = da.library()
+    fake = ctypes.c_void_p(0x10000)
+    P = plan(da, seq_q=4, causal=True)
+    assert lib.decode_attn_dense(ctypes.byref(P), fake, fake, fake, fake, 0.1, 3,
+                                 ctypes.c_void_p(0x20000), P.workspace_bytes, None) == 1
+    assert "query tokens" in da.decode_attn_last_error()
 
 
 def test_causal_is_accepted(da):
