@@ -89,11 +89,13 @@ def build_inputs(args, torch, W, H):
             table = None
             layout = f"contiguous cache, capacity {case.len_hi}"
         host = dict(q=q, k=k, v=v, sel=None, lens=lens, table=table)
+        toks = f", {case.seq_q} causal query tokens per sequence" if case.seq_q > 1 else ""
         desc = (f"{case.name}: dense decode with one length per sequence, B={case.B} "
-                f"Hq={case.Hq} Hkv={case.Hkv} D={case.D}, lengths {int(lens.min())}.."
+                f"Hq={case.Hq} Hkv={case.Hkv} D={case.D}{toks}, lengths {int(lens.min())}.."
                 f"{int(lens.max())} (sum {int(lens.sum())}), {layout}")
         cfg = dict(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
-                   max_k_len=case.len_hi, total_k_len=int(lens.sum()), page_size=case.page_size)
+                   max_k_len=case.len_hi, total_k_len=int(lens.sum()), page_size=case.page_size,
+                   seq_q=case.seq_q)
         return case, host, 2 * k.nbytes, desc, cfg, case.algorithmic_bytes()
     if args.workload in W.DENSE_CASES:
         case = W.DENSE_CASES[args.workload]
@@ -144,8 +146,11 @@ def cpu_baseline(args, case, host, algo_bytes, W):
                     vb = oracle.unpage(host["v"], host["table"][b:b + 1], rows_b)
                 else:
                     kb, vb = host["k"][b:b + 1], host["v"][b:b + 1]
-                oracle.dense(host["q"][b:b + 1], kb, vb, case.scale, int(host["lens"][b]),
-                             rows=heads, threads=threads)
+                for t in range(case.seq_q):
+                    seen = oracle.visible_keys(int(host["lens"][b]), case.seq_q, t, True)
+                    if seen > 0:
+                        oracle.dense(np.ascontiguousarray(host["q"][b:b + 1, :, t:t + 1]), kb, vb,
+                                     case.scale, seen, rows=heads, threads=threads)
         elif host["sel"] is None:
             oracle.dense(host["q"], host["k"], host["v"], case.scale, case.k_len, rows=rows,
                          threads=threads)
@@ -153,7 +158,7 @@ def cpu_baseline(args, case, host, algo_bytes, W):
             oracle.sparse(host["q"], host["k"], host["v"], host["sel"], case.scale, case.rows,
                           rows=rows, threads=threads)
         t_probe = time.perf_counter() - t0
-        if t_probe >= args.cpu_seconds or n >= rows_total * 4:
+        if t_probe >= args.cpu_seconds or n >= rows_total * 64:
             break
         grow = max(2.0, min(8.0, args.cpu_seconds / max(t_probe, 1e-3)))
         n = int(n * grow)
@@ -269,7 +274,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
-                             "paged", "select", "sparse_built"])
+                             "paged", "verify", "select", "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing of the plan-once call")
@@ -326,16 +331,17 @@ def main():
         dlens = H.to_dev_i32(host["lens"])
         dtable = H.to_dev_i32(host["table"]) if paged else None
     B, Hq, D = case.B, case.Hq, case.D
-    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, Hq, getattr(case, "seq_q", 1), D), dtype=torch.bfloat16, device="cuda")
     if ragged:
         cap = case.len_hi
         if paged:
             plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap, page_size=case.page_size,
                                        max_pages_per_seq=case.max_pages,
-                                       num_pages=host["k"].shape[0],
-                                       force_splits=args.force_splits)
+                                       num_pages=host["k"].shape[0], seq_q=case.seq_q,
+                                       causal=True, force_splits=args.force_splits)
         else:
             plan = da.decode_attn_plan(B, Hq, case.Hkv, D, cap, cap, ragged=True,
+                                       seq_q=case.seq_q, causal=True,
                                        force_splits=args.force_splits)
         splits = plan.balanced_wgs
     elif sparse:
@@ -473,7 +479,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "partial (split-K stream of K and V)",
+            "kernel": ("attend_balanced (length-balanced stream of K and V)" if ragged
+                       else "attend_partial (split-K stream of K and V)"),
             "kernel_us_mean": round(kern_mean_s * 1e6, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),

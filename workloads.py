@@ -26,6 +26,8 @@ follows the metrale page "AttnV41", decode_fixed_topk and decode_prep):
 * ``ragged``   B=32 Hq=32 Hkv=8 D=128, one live length per sequence: 32768
                for sequence 0, log-uniform in [512, 32768] for the rest
 * ``paged``    the same lengths over a paged cache of 64-row pages, shuffled
+* ``verify``   the ``ragged`` batch with 4 query tokens per sequence (causal: the
+               last 4 positions of each live prefix), as in verifying drafted tokens
 """
 
 from __future__ import annotations
@@ -241,6 +243,7 @@ class RaggedCase:
     len_hi: int             # also the capacity (rows per sequence) of the plan
     scale: float
     page_size: int = 0
+    seq_q: int = 1          # query tokens per sequence (causal, the last seq_q positions)
     std: float = 1.0
     seed: int = 0
 
@@ -259,7 +262,8 @@ class RaggedCase:
         """Live K+V rows of every sequence plus q and out (plus the block table if paged)."""
         n = int(self.lengths().sum())
         extra = self.B * self.max_pages * 4 if self.page_size else 0
-        return 2 * n * self.Hkv * self.D * 2 + 2 * (self.B * self.Hq * self.D * 2) + extra
+        return (2 * n * self.Hkv * self.D * 2 + 2 * (self.B * self.Hq * self.seq_q * self.D * 2)
+                + extra)
 
 
 RAGGED_CASES = {
@@ -267,6 +271,8 @@ RAGGED_CASES = {
                          seed=6),
     "paged": RaggedCase("paged", 32, 32, 8, 128, 512, 32768, _f32(1.0 / math.sqrt(128)),
                         page_size=64, seed=6),
+    "verify": RaggedCase("verify", 32, 32, 8, 128, 512, 32768, _f32(1.0 / math.sqrt(128)),
+                         seq_q=4, seed=6),
 }
 
 
@@ -301,22 +307,22 @@ def page_table(rng: np.random.Generator, lens, page_size: int, max_pages: int,
 
 
 def ragged_inputs(case: RaggedCase, seed: int | None = None):
-    """Contiguous layout: q [B,Hq,1,D], k, v [B,Hkv,len_hi,D], lengths [B] int32."""
+    """Contiguous layout: q [B,Hq,seq_q,D], k, v [B,Hkv,len_hi,D], lengths [B] int32."""
     sq, sk, sv, sl = seeds(case.seed if seed is None else seed)
-    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    q = normal_bf16(sq, (case.B, case.Hq, case.seq_q, case.D), case.std)
     k = normal_bf16(sk, (case.B, case.Hkv, case.len_hi, case.D), case.std)
     v = normal_bf16(sv, (case.B, case.Hkv, case.len_hi, case.D), case.std)
     return q, k, v, ragged_lengths(sl, case.B, case.len_lo, case.len_hi)
 
 
 def paged_inputs(case: RaggedCase, seed: int | None = None, spare: int = 0):
-    """Paged layout: q [B,Hq,1,D], k_pages, v_pages [num_pages,Hkv,page_size,D],
+    """Paged layout: q [B,Hq,seq_q,D], k_pages, v_pages [num_pages,Hkv,page_size,D],
     block table [B, max_pages] int32, lengths [B] int32."""
     sq, sk, sv, sl = seeds(case.seed if seed is None else seed)
     lens = ragged_lengths(sl, case.B, case.len_lo, case.len_hi)
     table, num_pages = page_table(np.random.Generator(np.random.PCG64(sl.spawn(1)[0])), lens,
                                   case.page_size, case.max_pages, spare)
-    q = normal_bf16(sq, (case.B, case.Hq, 1, case.D), case.std)
+    q = normal_bf16(sq, (case.B, case.Hq, case.seq_q, case.D), case.std)
     pool = (num_pages, case.Hkv, case.page_size, case.D)
     return q, normal_bf16(sk, pool, case.std), normal_bf16(sv, pool, case.std), table, lens
 
