@@ -178,6 +178,17 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   // are masked off before use. No row at or beyond k_len is ever read.
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kp);
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vp);
+  // Paged cache: the block-table entries of logical pages pg_first ..
+  // pg_first + 63 of sequence b, one per lane (-1 past the row), so a tile
+  // takes its page id with a lane read instead of a dependent load.
+  int pg_first = 0;
+  int pg_ids = -1;
+  auto load_page_ids = [&](int first) {
+    pg_first = first;
+    const int lp = first + lane;
+    pg_ids = lp < a.max_pages ? a.block_table[(int64_t)b * a.max_pages + lp] : -1;
+  };
+  if (!SPARSE && a.block_table) load_page_ids((int)((uint32_t)j0 / (uint32_t)a.page_size));
   auto load_tile = [&](TileRegs<D>& R, int tau) {
     const int64_t kt = j0 + (int64_t)tau * kTileKeys;
     R.tau = tau;
@@ -204,13 +215,18 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
         // Paged cache: a 32-key tile lies inside one page (tiles start at
         // multiples of 32, pages hold a multiple of 32 rows). A page id outside
         // [0, num_pages) is never read: the tile is dropped and its loads go to
-        // page 0.
-        const int64_t lp = base / a.page_size;
-        const int in_page = (int)(base - lp * a.page_size);
-        int64_t page = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + lp]);
-        if (page < 0 || page >= a.num_pages) {
-          page = 0;
-          R.mask = 0u;
+        // page 0, as do the loads of a tile with no key.
+        int64_t page = 0;
+        int in_page = 0;
+        if (n > 0) {
+          const int lp = (int)((uint32_t)kt / (uint32_t)a.page_size);  // kt < 2^31
+          in_page = (int)(kt - (int64_t)lp * a.page_size);
+          if (lp < pg_first || lp >= pg_first + 64) load_page_ids(lp);
+          page = __builtin_amdgcn_readlane(pg_ids, lp - pg_first);
+          if (page < 0 || page >= a.num_pages) {
+            page = 0;
+            R.mask = 0u;
+          }
         }
         const int64_t off = ((page * a.Hkv + hkv) * a.page_size + in_page) * Gm::ROWB;
         kb = reinterpret_cast<const unsigned char*>(a.k) + off;
