@@ -705,66 +705,80 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
     *reinterpret_cast<uint2*>(out) = make_uint2(w4[0], w4[1]);
 }
 
-// Log-sum-exp merge of the S split partials of one output row per workgroup.
-// M = max_s m_s; wave w accumulates the splits s = w, w + 4, ... with weights
-// 2^(m_s - M) (0 for an empty split, whose partial holds zeros); the four
-// waves are then summed in a fixed order. With one non-empty split its weight
-// is exactly 1 and every other term is an exact 0, so the result equals the
-// one-split output bit for bit.
+// Log-sum-exp merge of the S split partials: one wave per output row, four rows
+// per workgroup, lane l owning D/64 output values. With at most kFastSplits
+// splits every load (the running maxima, denominators and partial outputs of
+// all splits; rows past the last split re-read it and get weight 0) is issued
+// before any is used, so the merge costs about one memory round trip; more
+// splits run the same arithmetic in a loop. M = max_s m_s, weights 2^(m_s - M)
+// (exactly 0 for an empty split, whose partial holds zeros), sums in split
+// order. With one non-empty split its weight is exactly 1 and every other term
+// an exact 0, so the result equals the one-split output bit for bit.
+constexpr int kFastSplits = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
   constexpr int PER = D / 64;  // outputs per lane
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole waves leave
   const int S = a.S;
   const float* pm = a.part_m + row * S;
   const float* pl = a.part_l + row * S;
   const float* po = a.part_o + row * S * D + lane * PER;
-  __shared__ float red_m[4];
-  __shared__ float red_l[4];
-  __shared__ float red_o[4][D];
 
-  float M = kNegInf;
-  for (int j = tid; j < S; j += 256) M = fmaxf(M, pm[j]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float L = 0.f, acc[PER];
+  float M = kNegInf, L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  if (M != kNegInf) {
-#pragma unroll 4
-    for (int j = wave; j < S; j += 4) {
-      const float mj = pm[j];
-      const float w = (mj == kNegInf) ? 0.f : exp2_fast(mj - M);
-      L += pl[j] * w;
-      const float* src = po + (int64_t)j * D;
+  if (S <= kFastSplits) {
+    float m[kFastSplits], l[kFastSplits], o[kFastSplits][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += src[e] * w;
+    for (int s = 0; s < kFastSplits; ++s) {
+      const int j = s < S ? s : S - 1;
+      m[s] = pm[j];
+      l[s] = pl[j];
+      if constexpr (PER == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(po + (int64_t)j * D);
+        o[s][0] = v.x;
+        o[s][1] = v.y;
+      } else {
+        o[s][0] = po[(int64_t)j * D];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kFastSplits; ++s) {
+      if (s >= S) m[s] = kNegInf;
+      M = fmaxf(M, m[s]);
+    }
+    if (M != kNegInf) {
+#pragma unroll
+      for (int s = 0; s < kFastSplits; ++s) {
+        const float w = exp2_fast(m[s] - M);
+        L += l[s] * w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += o[s][e] * w;
+      }
+    }
+  } else {
+    for (int j = lane; j < S; j += 64) M = fmaxf(M, pm[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (M != kNegInf) {
+#pragma unroll 8
+      for (int j = 0; j < S; ++j) {
+        const float w = exp2_fast(pm[j] - M);
+        L += pl[j] * w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += po[(int64_t)j * D + e] * w;
+      }
     }
   }
-  if (lane == 0) red_l[wave] = L;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) red_o[wave][lane * PER + e] = acc[e];
-  __syncthreads();
-  if (wave == 0) {
-    L = ((red_l[0] + red_l[1]) + red_l[2]) + red_l[3];
-    const float inv = (L > 0.f) ? 1.f / L : 0.f;
-    float o[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = lane * PER + e;
-      o[e] = (((red_o[0][d] + red_o[1][d]) + red_o[2][d]) + red_o[3][d]) * inv;
-    }
-    if constexpr (PER == 2)
-      *reinterpret_cast<uint32_t*>(a.out + row * D + lane * 2) = pack_bf16(o[0], o[1]);
-    else
-      a.out[row * D + lane] = (uint16_t)(pack_bf16(o[0], 0.f) & 0xffffu);
-  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  if constexpr (PER == 2)
+    *reinterpret_cast<uint32_t*>(a.out + row * D + lane * 2) = pack_bf16(acc[0] * inv, acc[1] * inv);
+  else
+    a.out[row * D + lane] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
 }
 
 template <int D, bool SPARSE>
@@ -826,11 +840,12 @@ hipError_t launch_partial(const PartialLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream) {
   const int64_t rows = (int64_t)L.B * L.Hq * L.Sq;
-  if (rows <= 0 || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (rows <= 0 || rows > 0x7fffffff || L.S < 1) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)((rows + 3) / 4);  // one wave per row
   if (L.D == 128)
-    hipLaunchKernelGGL(combine_splits<128>, dim3((unsigned)rows), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<128>, dim3(grid), dim3(256), 0, stream, L);
   else if (L.D == 64)
-    hipLaunchKernelGGL(combine_splits<64>, dim3((unsigned)rows), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(combine_splits<64>, dim3(grid), dim3(256), 0, stream, L);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
