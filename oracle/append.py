@@ -9,6 +9,11 @@ on the device). Readings (listed in the design notes): with window == 0 the row
 is ``pos``; otherwise it is ``win_base + pos % window``; a position that is
 negative or lands outside ``[0, capacity)`` writes nothing.
 
+Several new rows per sequence (``append_rows``: the tokens of a pass are the
+last positions of the live prefix) and a paged cache written through a block
+table (``append_paged``; the metrale page "DflashScratch" writes its cache
+through slot indices) compose the same single-row write.
+
 Plain numpy indexing, one row at a time. Pinned by ``tests/test_append_oracle.py``.
 """
 
@@ -34,4 +39,41 @@ def append_kv(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
         for h in range(Hkv):
             k[b, h, row, :] = k_new[b, h, 0, :]
             v[b, h, row, :] = v_new[b, h, 0, :]
+    return k, v
+
+
+def append_rows(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                k_lens):
+    """Several new rows per sequence at the end of its live prefix: the live
+    length counts them (DecodeFlashSpec, field k_len), so with k_new
+    [B, Hkv, Sq, D] row t of sequence b goes to cache row k_lens[b] - Sq + t (a
+    negative row writes nothing). One append_kv per new row."""
+    Sq = k_new.shape[2]
+    k, v = k_cache, v_cache
+    for t in range(Sq):
+        pos = [int(n) - Sq + t for n in k_lens]
+        k, v = append_kv(k, v, k_new[:, :, t:t + 1], v_new[:, :, t:t + 1], pos)
+    return k, v
+
+
+def append_paged(k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                 k_new: np.ndarray, v_new: np.ndarray, k_lens):
+    """append_rows through a block table: logical row r of sequence b is row
+    r % page_size of page block_table[b, r // page_size] of the pools
+    [num_pages, Hkv, page_size, D]. A negative row, or a page id outside the
+    pool, writes nothing."""
+    k = k_pages.copy()
+    v = v_pages.copy()
+    num_pages, Hkv, page_size, D = k.shape
+    B, _, Sq, _ = k_new.shape
+    for b in range(B):
+        for t in range(Sq):
+            r = int(k_lens[b]) - Sq + t
+            if r < 0:
+                continue
+            pg = int(block_table[b, r // page_size])
+            if pg < 0 or pg >= num_pages:
+                continue
+            k[pg, :, r % page_size, :] = k_new[b, :, t, :]
+            v[pg, :, r % page_size, :] = v_new[b, :, t, :]
     return k, v
