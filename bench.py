@@ -285,6 +285,10 @@ def main():
     ap.add_argument("--with-append", action="store_true",
                     help="dense: each step first appends the token's K/V rows at k_len - 1 "
                          "(a whole decode step: append, then attend)")
+    ap.add_argument("--step", action="store_true",
+                    help="dense: each step is one decode_attn_dense_step call, which writes the "
+                         "pass's new K/V rows at the end of each prefix and attends (one kernel "
+                         "pair instead of append + attention)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -355,16 +359,33 @@ def main():
     ws = da.workspace_for(plan)
 
     append = args.with_append and not sparse and not ragged
-    if append:
+    one_call = args.step and not sparse
+    if args.step and sparse:
+        print("--step applies to the dense workloads", file=sys.stderr)
+        sys.exit(2)
+    Sq = getattr(case, "seq_q", 1)
+    if append or one_call:
         rng = np.random.Generator(np.random.PCG64(7))
-        kn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal((B, case.Hkv, 1, D), np.float32)))
-        vn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal((B, case.Hkv, 1, D), np.float32)))
+        nshape = (B, case.Hkv, Sq if one_call else 1, D)
+        kn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
+        vn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
+        algo_bytes += 2 * 2 * B * case.Hkv * nshape[2] * D * 2  # new rows read and written
+    if append:
         pos_dev = torch.full((B,), case.k_len - 1, dtype=torch.int32, device="cuda")
-        algo_bytes += 2 * 2 * B * case.Hkv * D * 2  # new rows read and written
+    if one_call and not ragged:
+        # fixed-length workloads: every sequence at k_len, through the length-balanced kernel
+        plan = da.decode_attn_plan(B, Hq, case.Hkv, D, case.capacity, case.k_len, ragged=True)
+        ws = da.workspace_for(plan)
+        dlens = torch.full((B,), case.k_len, dtype=torch.int32, device="cuda")
+        dtable = None
+        splits = plan.balanced_wgs
 
     def step(i):
         kk, vv = dks[i % sets], dvs[i % sets]
-        if paged:
+        if one_call:
+            da.decode_attn_dense_step(plan, dq, kk, vv, kn, vn, dlens, out, case.scale,
+                                      block_table=dtable if paged else None, workspace=ws)
+        elif paged:
             da.decode_attn_dense_paged(plan, dq, kk, vv, dtable, dlens, out, case.scale,
                                        workspace=ws)
         elif ragged:
@@ -416,7 +437,7 @@ def main():
 
         def gstep(i):
             kk, vv = dks[i % sets], dvs[i % sets]
-            if ragged:
+            if ragged or one_call:
                 step(i)
             elif sparse:
                 da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows,
@@ -453,7 +474,7 @@ def main():
         log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
         del src, dst
 
-    traffic = traffic_from_counters(args.workload)
+    traffic = traffic_from_counters(args.workload + ("+step" if one_call else ""))
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -469,7 +490,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(workload=desc + (" (+ KV append per step)" if append else ""),
+        "config": dict(workload=desc + (" (+ KV append per step)" if append else "")
+                       + (" (one-call step: new rows written, then attended)" if one_call else ""),
                        splits=splits, kv_sets=sets,
                        algorithmic_bytes_per_step=algo_bytes, **cfg),
         "roofline": {
@@ -479,7 +501,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": ("attend_balanced (length-balanced stream of K and V)" if ragged
+            "kernel": ("attend_balanced (length-balanced stream of K and V)" if ragged or one_call
                        else "attend_partial (split-K stream of K and V)"),
             "kernel_us_mean": round(kern_mean_s * 1e6, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),

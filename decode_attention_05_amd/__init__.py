@@ -20,7 +20,7 @@ import os
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_dense_ragged",
-    "decode_attn_dense_paged", "decode_attn_sparse",
+    "decode_attn_dense_paged", "decode_attn_dense_step", "decode_attn_sparse",
     "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
     "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
     "workspace_for",
@@ -33,7 +33,7 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
 EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
-                    "decode_attn_dense_ragged", "decode_attn_dense_paged",
+                    "decode_attn_dense_ragged", "decode_attn_dense_paged", "decode_attn_dense_step",
                     "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
@@ -120,6 +120,10 @@ def library():
                                                 ctypes.c_int32, P, ctypes.c_float, P,
                                                 ctypes.c_size_t, P]
         lib.decode_attn_dense_paged.restype = ctypes.c_int
+        lib.decode_attn_dense_step.argtypes = [ctypes.POINTER(Plan), P, P, P, P, P, P, P,
+                                               ctypes.c_int32, P, ctypes.c_float, P,
+                                               ctypes.c_size_t, P]
+        lib.decode_attn_dense_step.restype = ctypes.c_int
         lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
                                            ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_sparse.restype = ctypes.c_int
@@ -302,6 +306,38 @@ def decode_attn_dense_paged(plan: Plan, q, k_pages, v_pages, block_table, k_lens
     _check(library().decode_attn_dense_paged(ctypes.byref(plan), qp, kp, vp, bt, lens,
                                              int(k_lens_stride), op, float(softmax_scale), ws, wsb,
                                              _stream_ptr(stream)))
+    return out
+
+
+def decode_attn_dense_step(plan: Plan, q, k_cache, v_cache, k_new, v_new, k_lens, out,
+                           softmax_scale: float, block_table=None, k_lens_stride: int = 1,
+                           workspace=None, stream=None):
+    """Write the pass's new K/V rows [B, Hkv, Sq, D] at rows [k_len - Sq, k_len) of
+    each sequence's cache and attend, in one call (contiguous caches with a
+    ragged plan, or page pools with a paged plan and ``block_table``)."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, Sq = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.seq_q
+    bf = torch.bfloat16
+    if p.page_size > 0:
+        shape = (p.num_pages, Hkv, p.page_size, D)
+        bt = _tensor_ptr(block_table, "block_table", (B, p.max_pages_per_seq), torch.int32)
+    else:
+        shape = (B, Hkv, p.capacity, D)
+        if block_table is not None:
+            raise ValueError("block_table is for paged plans")
+        bt = None
+    qp = _tensor_ptr(q, "q", (B, Hq, Sq, D), bf)
+    kc = _tensor_ptr(k_cache, "k_cache", shape, bf)
+    vc = _tensor_ptr(v_cache, "v_cache", shape, bf)
+    kn = _tensor_ptr(k_new, "k_new", (B, Hkv, Sq, D), bf)
+    vn = _tensor_ptr(v_new, "v_new", (B, Hkv, Sq, D), bf)
+    lens = _lens_ptr(k_lens, B, k_lens_stride)
+    op = _tensor_ptr(out, "out", (B, Hq, Sq, D), bf)
+    ws, wsb = _ws_ptr(plan, workspace)
+    _check(library().decode_attn_dense_step(ctypes.byref(plan), qp, kc, vc, kn, vn, bt, lens,
+                                            int(k_lens_stride), op, float(softmax_scale), ws, wsb,
+                                            _stream_ptr(stream)))
     return out
 
 

@@ -293,7 +293,8 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
                                       const void* k, const void* v, const int32_t* block_table,
                                       const int32_t* k_lens, int32_t k_lens_stride, void* out,
                                       float softmax_scale, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      size_t workspace_bytes, void* stream,
+                                      const void* k_new = nullptr, const void* v_new = nullptr) {
   decode_attn_status s =
       check_common(plan, 0, q, k, v, out, softmax_scale, workspace, workspace_bytes);
   if (s != DA_OK) return s;
@@ -326,6 +327,30 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (k_new) {
+    // The pass's new rows first (one small kernel), then the attention reads
+    // them from the cache like every other row.
+    da::AppendRowsLaunch A{};
+    A.k_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(k));
+    A.v_cache = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
+    A.k_new = static_cast<const uint16_t*>(k_new);
+    A.v_new = static_cast<const uint16_t*>(v_new);
+    A.k_lens = k_lens;
+    A.k_lens_stride = k_lens_stride;
+    A.max_len = plan->prob.max_k_len;
+    A.block_table = block_table;
+    A.page_size = plan->prob.page_size;
+    A.max_pages = plan->prob.max_pages_per_seq;
+    A.num_pages = plan->prob.num_pages;
+    A.B = plan->prob.batch;
+    A.Hkv = plan->prob.num_kv_heads;
+    A.Sq = plan->prob.seq_q;
+    A.D = plan->prob.head_dim;
+    A.capacity = plan->prob.capacity;
+    e = da::launch_append_rows(A, st);
+    if (e != hipSuccess)
+      return fail(DA_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
+  }
   if (g_ev_before) {
     e = hipEventRecord(g_ev_before, st);
     if (e != hipSuccess) return fail(DA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
@@ -466,6 +491,19 @@ decode_attn_status decode_attn_dense_ragged(const decode_attn_plan_t* plan, cons
                                             size_t workspace_bytes, void* stream) {
   return dense_with_lengths(plan, q, k, v, nullptr, k_lens, k_lens_stride, out, softmax_scale,
                             workspace, workspace_bytes, stream);
+}
+
+decode_attn_status decode_attn_dense_step(const decode_attn_plan_t* plan, const void* q,
+                                          void* k_cache, void* v_cache, const void* k_new,
+                                          const void* v_new, const int32_t* block_table,
+                                          const int32_t* k_lens, int32_t k_lens_stride, void* out,
+                                          float softmax_scale, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return fail(DA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(DA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return dense_with_lengths(plan, q, k_cache, v_cache, block_table, k_lens, k_lens_stride, out,
+                            softmax_scale, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 decode_attn_status decode_attn_dense_paged(const decode_attn_plan_t* plan, const void* q,

@@ -20,4 +20,24 @@ struct AppendLaunch {
 
 hipError_t launch_append(const AppendLaunch& L, hipStream_t stream);
 
+// The Sq new rows of each sequence at the end of its live prefix: row t of
+// sequence b goes to row clamp(k_lens[b * k_lens_stride], 0, max_len) - Sq + t
+// of a contiguous cache, or through a block table into page pools.
+struct AppendRowsLaunch {
+  uint16_t* k_cache;        // [B, Hkv, capacity, D] bf16, or pools [num_pages, Hkv, page_size, D]
+  uint16_t* v_cache;
+  const uint16_t* k_new;    // [B, Hkv, Sq, D] bf16
+  const uint16_t* v_new;
+  const int32_t* k_lens;    // device lengths, counting the new rows
+  int k_lens_stride;
+  int64_t max_len;          // lengths are clamped to [0, max_len]
+  const int32_t* block_table;  // paged: [B, max_pages] page ids, else null
+  int page_size, max_pages;
+  int64_t num_pages;
+  int B, Hkv, Sq, D;
+  int64_t capacity;
+};
+
+hipError_t launch_append_rows(const AppendRowsLaunch& L, hipStream_t stream);
+
 }  // namespace da

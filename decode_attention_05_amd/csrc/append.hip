@@ -9,7 +9,9 @@
 // next to the attention call. A position that is negative or lands outside the
 // cache writes nothing.
 //
-// One thread per 16-byte chunk of a (token, kv head, K or V) row.
+// One thread per 16-byte chunk of a (token, kv head, K or V) row. The rows of
+// a one-call decode pass (several new rows per sequence, at the end of its
+// live prefix read on the device, contiguous or paged) use append_rows_kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,7 +42,47 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendLaunch a) {
   *dst = *src;
 }
 
+// One thread per 16-byte chunk of a (sequence, kv head, new row, K or V) row. A
+// row before the start of the cache (a length below Sq) or on a page id
+// outside the pool is not written.
+__global__ __launch_bounds__(256) void append_rows_kernel(AppendRowsLaunch a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int chunks = a.D / 8;
+  const int64_t per_side = (int64_t)a.B * a.Hkv * a.Sq * chunks;
+  if (t >= 2 * per_side) return;
+  const int which = (int)(t / per_side);  // 0: K, 1: V
+  int64_t r = t % per_side;
+  const int c = (int)(r % chunks);
+  r /= chunks;
+  const int s = (int)(r % a.Sq);
+  const int64_t bh = r / a.Sq;            // b * Hkv + h
+  const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+  int64_t len = a.k_lens[(int64_t)b * a.k_lens_stride];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int64_t row = len - a.Sq + s;
+  if (row < 0) return;
+  int64_t dst_row;
+  if (a.block_table) {
+    const int64_t page = a.block_table[(int64_t)b * a.max_pages + row / a.page_size];
+    if (page < 0 || page >= a.num_pages) return;
+    dst_row = (page * a.Hkv + h) * a.page_size + row % a.page_size;
+  } else {
+    dst_row = bh * a.capacity + row;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(which ? a.v_new : a.k_new) + r * chunks + c;
+  uint4* dst = reinterpret_cast<uint4*>(which ? a.v_cache : a.k_cache) + dst_row * chunks + c;
+  *dst = *src;
+}
+
 }  // namespace
+
+hipError_t launch_append_rows(const AppendRowsLaunch& L, hipStream_t stream) {
+  const int64_t total = 2 * (int64_t)L.B * L.Hkv * L.Sq * (L.D / 8);
+  const int64_t blocks = (total + 255) / 256;
+  if (total <= 0 || blocks > 0x7fffffff || L.D % 8 != 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendLaunch& L, hipStream_t stream) {
   const int64_t total = 2 * (int64_t)L.B * L.Hkv * (L.D / 8);

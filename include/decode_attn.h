@@ -201,6 +201,34 @@ decode_attn_status decode_attn_dense_paged(const decode_attn_plan_t* plan, const
                                            void* stream);
 
 /*
+ * One whole dense decode pass in a single call: write the pass's new K and V
+ * rows into the cache and attend (the append-then-attend step of plan-once
+ * decode: the live length counts the new tokens, fuel-dispatch page
+ * "DecodeFlashSpec", field k_len; the metrale page "DflashScratch" writes its
+ * cache through slot indices). Needs a plan made with ragged = 1 (contiguous
+ * cache, block_table NULL) or a paged plan (block_table as
+ * decode_attn_dense_paged).
+ *   k_cache, v_cache  the caches of decode_attn_dense_ragged / _paged (written).
+ *   k_new, v_new  [B, Hkv, Sq, D] bf16: row t of sequence b belongs at cache row
+ *          L_b - Sq + t, L_b = clamp(k_lens[b * k_lens_stride], 0, max_k_len).
+ *          Those rows are written (a negative row, or one whose page id lies
+ *          outside the pool, is not), and token t attends [0, L_b) or its
+ *          causal part, reading them as written.
+ *   the other arguments as decode_attn_dense_ragged / decode_attn_dense_paged.
+ * Enqueues a small row-write kernel and then the attention kernels of
+ * decode_attn_dense_ragged / _paged, so the result equals those calls made
+ * after writing the rows, bit for bit. (Measured: folding the write into the
+ * attention kernel cost more than the extra launch.)
+ * Returns as decode_attn_dense.
+ */
+decode_attn_status decode_attn_dense_step(const decode_attn_plan_t* plan, const void* q,
+                                          void* k_cache, void* v_cache, const void* k_new,
+                                          const void* v_new, const int32_t* block_table,
+                                          const int32_t* k_lens, int32_t k_lens_stride, void* out,
+                                          float softmax_scale, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * Index-selected sparse decode attention.
  *   q    [B, Hq, 1, D] bf16           k, v [kv_batch, Hkv, capacity, D] bf16
  *   sel  [B, topk] int32 (device): token b attends rows sel[b, t] of its KV set

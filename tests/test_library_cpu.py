@@ -302,6 +302,15 @@ def test_ragged_and_paged_fail_closed(da):
     assert pag(G, bt=ctypes.c_void_p(0x10002)) == 1
     assert pag(G, lens=None) == 1
     assert pag(G, stride=-3) == 1
+    # the one-call decode pass: new rows required and aligned, plans as above
+    step = lambda pl, kn=fake, vn=fake, bt=None: lib.decode_attn_dense_step(  # noqa: E731
+        ctypes.byref(pl), fake, fake, fake, kn, vn, bt, fake, 1, fake, 0.1, ws, pl.workspace_bytes,
+        None)
+    assert step(P, kn=None) == 1
+    assert step(P, vn=ctypes.c_void_p(0x10008)) == 1
+    assert step(D) == 1                 # not a ragged plan
+    assert step(G) == 1                 # a paged plan without a block table
+    assert step(P, bt=fake) == 1        # a block table with a contiguous plan
     # the fixed-length calls refuse a paged plan
     assert lib.decode_attn_dense(ctypes.byref(G), fake, fake, fake, fake, 0.1, 10, ws,
                                  G.workspace_bytes, None) == 1
