@@ -14,7 +14,15 @@
 // with a host-side top-k out of a captured graph.
 //
 // One 1024-thread workgroup per token. Scores become 32-bit totalOrder keys.
-//   1. Two histogram passes over the scores (8 bits each, from the top) find
+//   0. Prefilter (at least 8192 candidates): 256 runs of 8 keys spread over
+//      the row are sampled, and the lower end of the 16-bit bucket of the
+//      sample key a few standard deviations beyond the expected rank of the
+//      k-th largest key becomes a bound L0. One pass keeps every key >= L0 in
+//      LDS (a wave scan and one LDS atomic per wave per chunk place them). If
+//      at least k keys were kept (so the k-th largest key is >= L0 and the top
+//      k are all among them) and they fit, steps 1-2 run on the kept keys,
+//      otherwise on all keys: the result is exact either way.
+//   1. Two histogram passes over the key set (8 bits each, from the top) find
 //      the 16-bit key bucket that holds the k-th largest key, how many keys lie
 //      above that bucket and how many inside it. Each thread keeps 8 16-byte
 //      loads in flight; counts go to 16 lane-striped LDS histograms plus spare
@@ -47,6 +55,10 @@ constexpr int kBins = 256 + 32 + 1;        // 256 digits, 32 spare bins for non-
 constexpr int kLoads = 8;                  // 16-byte loads in flight per thread in a pass
 constexpr int kCandCap = 2048;             // candidate list (keys inside the threshold bucket)
 constexpr int kWords = kSelectMaxCandidates / 32;  // bitmap of the candidate rows
+constexpr int kSampleRuns = 256;           // the prefilter's sample: 256 runs of 8 keys
+constexpr int kSample = 8 * kSampleRuns;
+constexpr int kPreCap = 8192;              // keys kept by the prefilter
+constexpr int kPreMinN = 8192;             // rows below this go straight to the exact path
 
 // IEEE 754 totalOrder as an unsigned key: larger float -> larger key.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -63,8 +75,10 @@ struct Shared {
   uint32_t hist[kCopies][kBins];
   uint32_t bitmap[kWords];     // bit i: candidate row i is selected
   uint64_t cand[kCandCap];     // keys inside the threshold bucket
+  uint64_t pre[kPreCap];       // prefilter: the (key, row) items at or above the bound
+  uint32_t sample[kSample];    // prefilter: sampled keys
   uint32_t wsum[kSelWaves];
-  uint32_t prefix, need, count, n_cand, cut;
+  uint32_t prefix, need, count, n_cand, cut, n_pre;
 };
 
 // A pass visits the scores in chunks of kSelThreads * kLoads * 4 elements: the
@@ -124,7 +138,9 @@ __device__ __forceinline__ void for_each_key(const float* sc, int n, Fn fn) {
 // Digit histogram (bits shift .. shift+7) of the keys matching prefix under mask,
 // then choice of the digit that holds the need-th largest matching key.
 // Updates prefix/mask/need; returns the count of keys in the chosen digit.
-__device__ uint32_t radix_pass(const float* sc, int n, int shift, uint32_t& prefix, uint32_t& mask,
+// `visit(fn)` calls fn(key, row, live) for every key of the set.
+template <class Visit>
+__device__ uint32_t radix_pass(Visit&& visit, int shift, uint32_t& prefix, uint32_t& mask,
                                uint32_t& need, Shared& S) {
   const int tid = threadIdx.x;
   // Lane l counts into copy l % 16, so at most the 4 lanes l, l+16, l+32, l+48
@@ -135,7 +151,7 @@ __device__ uint32_t radix_pass(const float* sc, int n, int shift, uint32_t& pref
   for (int i = tid; i < kCopies * kBins; i += kSelThreads) (&S.hist[0][0])[i] = 0u;
   __syncthreads();
   const uint32_t spare = 256u + (uint32_t)((tid >> 4) & 31);
-  for_each_key(sc, n, [&](uint32_t key, uint32_t, bool live) {
+  visit([&](uint32_t key, uint32_t, bool live) {
     const bool hit = live && (key & mask) == prefix;
     atomicAdd(&S.hist[copy][hit ? (key >> shift) & 255u : spare], 1u);
   });
@@ -229,44 +245,27 @@ __device__ __forceinline__ void mark(Shared& S, uint32_t i) {
   atomicOr(&S.bitmap[i >> 5], 1u << (i & 31u));
 }
 
-__global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaunch a) {
-  __shared__ Shared S;
-  const int b = blockIdx.x;
+// The k largest keys of the set `visit` enumerates (ties to the lower row)
+// marked in the bitmap: two radix passes find the 16-bit bucket of the k-th
+// largest key; rows above it are marked and the keys inside it are collected
+// and sorted, unless the bucket holds more keys than the candidate list, in
+// which case an exact 4-pass radix select finds the threshold key and the cut
+// row among the keys equal to it. Every thread of the workgroup calls it.
+template <class Visit>
+__device__ void exact_select(Visit&& visit, int k, int nwords, Shared& S) {
   const int tid = threadIdx.x;
-  const float* sc = a.scores + (int64_t)b * a.score_stride;
-  int32_t* out = a.sel + (int64_t)b * a.topk;
-
-  const int pos = a.pos[b];
-  int n_win = 0;
-  if (a.window > 0 && pos >= 0) n_win = pos + 1 < a.window ? pos + 1 : a.window;
-  if (n_win > a.topk) n_win = a.topk;
-  int k = a.k_idx < a.n_idx ? a.k_idx : a.n_idx;
-  if (k > a.topk - n_win) k = a.topk - n_win;
-  if (k < 0) k = 0;
-  for (int j = tid; j < a.topk; j += kSelThreads) {
-    if (j < n_win) {
-      const int p = pos - n_win + 1 + j;  // >= 0
-      out[j] = (int32_t)(a.win_base + p % a.window);
-    } else if (j >= n_win + k) {
-      out[j] = -1;
-    }
-  }
-  if (k == 0) return;
-  const int n = a.n_idx;
-  const int nwords = (n + 31) >> 5;
-
-  // 1. The 16-bit bucket of the k-th largest key.
+  // The 16-bit bucket of the k-th largest key.
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
-  radix_pass(sc, n, 24, prefix, mask, need, S);
-  const uint32_t in_bucket = radix_pass(sc, n, 16, prefix, mask, need, S);
+  radix_pass(visit, 24, prefix, mask, need, S);
+  const uint32_t in_bucket = radix_pass(visit, 16, prefix, mask, need, S);
   const uint32_t top16 = prefix >> 16;
   for (int w = tid; w < nwords; w += kSelThreads) S.bitmap[w] = 0u;
   if (tid == 0) S.n_cand = 0u;
   __syncthreads();
 
   if (in_bucket <= (uint32_t)kCandCap) {
-    // 2. Rows above the bucket are selected outright; keys inside it are candidates.
-    for_each_key(sc, n, [&](uint32_t key, uint32_t i, bool live) {
+    // Rows above the bucket are selected outright; keys inside it are candidates.
+    visit([&](uint32_t key, uint32_t i, bool live) {
       if (!live) return;
       const uint32_t hi = key >> 16;
       if (hi > top16) mark(S, i);
@@ -302,10 +301,10 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
   } else {
     // Heavily tied scores: the exact threshold key T, then the cut index I, the
     // need-th lowest index among the keys equal to T.
-    radix_pass(sc, n, 8, prefix, mask, need, S);
-    radix_pass(sc, n, 0, prefix, mask, need, S);
+    radix_pass(visit, 8, prefix, mask, need, S);
+    radix_pass(visit, 0, prefix, mask, need, S);
     const uint32_t T = prefix;
-    for_each_key(sc, n, [&](uint32_t key, uint32_t i, bool live) {
+    visit([&](uint32_t key, uint32_t i, bool live) {
       if (live && key == T) mark(S, i);
     });
     __syncthreads();
@@ -330,11 +329,132 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
     const uint32_t I = S.cut;
     for (int w = tid; w < nwords; w += kSelThreads) S.bitmap[w] = 0u;
     __syncthreads();
-    for_each_key(sc, n, [&](uint32_t key, uint32_t i, bool live) {
+    visit([&](uint32_t key, uint32_t i, bool live) {
       if (live && (key > T || (key == T && i <= I))) mark(S, i);
     });
   }
   __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaunch a) {
+  __shared__ Shared S;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  int32_t* out = a.sel + (int64_t)b * a.topk;
+
+  const int pos = a.pos[b];
+  int n_win = 0;
+  if (a.window > 0 && pos >= 0) n_win = pos + 1 < a.window ? pos + 1 : a.window;
+  if (n_win > a.topk) n_win = a.topk;
+  int k = a.k_idx < a.n_idx ? a.k_idx : a.n_idx;
+  if (k > a.topk - n_win) k = a.topk - n_win;
+  if (k < 0) k = 0;
+  for (int j = tid; j < a.topk; j += kSelThreads) {
+    if (j < n_win) {
+      const int p = pos - n_win + 1 + j;  // >= 0
+      out[j] = (int32_t)(a.win_base + p % a.window);
+    } else if (j >= n_win + k) {
+      out[j] = -1;
+    }
+  }
+  if (k == 0) return;
+  const int n = a.n_idx;
+  const int nwords = (n + 31) >> 5;
+
+  // 1. Prefilter (rows >= kPreMinN): a sample of the keys gives a lower bound
+  //    L0 meant to lie below the k-th largest key; one pass keeps every key
+  //    >= L0. When at least k keys were kept (so the k-th largest key is
+  //    >= L0 and the top k are all among them) and they fit, the exact
+  //    selection runs on the kept keys in LDS; otherwise on all keys. Either
+  //    way the result is exact; the sample only decides how fast.
+  bool use_pre = false;
+  if (n >= kPreMinN) {
+    if (tid < 2 * kSampleRuns) {
+      const int run = tid >> 1;
+      const int64_t start = ((int64_t)run * (n - 8) / (kSampleRuns - 1)) & ~(int64_t)3;
+      const float4 f = *reinterpret_cast<const float4*>(sc + start + 4 * (tid & 1));
+      S.sample[4 * tid + 0] = order_key(f.x);
+      S.sample[4 * tid + 1] = order_key(f.y);
+      S.sample[4 * tid + 2] = order_key(f.z);
+      S.sample[4 * tid + 3] = order_key(f.w);
+    }
+    if (tid == 0) S.n_pre = 0u;
+    __syncthreads();
+    // The k-th largest key sits near sample rank k * kSample / n; go four
+    // standard deviations (plus a margin) deeper and take the lower end of
+    // that key's 16-bit bucket.
+    const int mu = (int)(((int64_t)k * kSample) / n);
+    int r0 = mu + 4 * ((int)sqrtf((float)mu) + 1) + 8;
+    if (r0 > kSample - 1) r0 = kSample - 1;
+    if ((int64_t)(r0 + 1) * n <= (int64_t)kPreCap * kSample * 3 / 4) {  // expected keep fits
+      auto visit_sample = [&](auto fn) {
+        for (int i = tid; i < kSample; i += kSelThreads) fn(S.sample[i], (uint32_t)i, true);
+      };
+      uint32_t sp = 0u, sm = 0u, sneed = (uint32_t)(r0 + 1);
+      radix_pass(visit_sample, 24, sp, sm, sneed, S);
+      radix_pass(visit_sample, 16, sp, sm, sneed, S);
+      const uint32_t L0 = sp;  // low 16 bits are zero: the bucket's smallest key
+      const int lane = tid & 63;
+      // Per chunk, each lane counts its kept keys, a wave scan gives each lane
+      // its offset, and one LDS atomic per wave reserves the wave's space.
+      const int nv = n >> 2;
+      for (int vbase = 0; vbase < nv; vbase += kSelThreads * kLoads) {
+        Chunk c;
+        load_chunk(sc, nv, vbase, c);
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cnt += (c.valid[u] && c.key[u][e] >= L0) ? 1u : 0u;
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        uint32_t base = 0u;
+        if (lane == 63) base = atomicAdd(&S.n_pre, incl);
+        uint32_t pos = __shfl(base, 63) + incl - cnt;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+          const uint32_t i0 = 4u * (uint32_t)(vbase + tid + kSelThreads * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (c.valid[u] && c.key[u][e] >= L0) {
+              if (pos < (uint32_t)kPreCap) S.pre[pos] = sort_item(c.key[u][e], i0 + e);
+              ++pos;
+            }
+          }
+        }
+      }
+      const int tail = n & 3;
+      if (tid < tail) {
+        const int i = 4 * nv + tid;
+        const uint32_t key = order_key(sc[i]);
+        if (key >= L0) {
+          const uint32_t pos = atomicAdd(&S.n_pre, 1u);
+          if (pos < (uint32_t)kPreCap) S.pre[pos] = sort_item(key, (uint32_t)i);
+        }
+      }
+      __syncthreads();
+      const uint32_t kept = S.n_pre;
+      use_pre = kept >= (uint32_t)k && kept <= (uint32_t)kPreCap;
+    }
+  }
+
+  // 2. Exact selection of the top k of the chosen key set into the bitmap.
+  if (use_pre) {
+    const int kept = (int)S.n_pre;
+    exact_select([&](auto fn) {
+      for (int i = tid; i < kept; i += kSelThreads) {
+        const uint64_t it = S.pre[i];
+        fn(~(uint32_t)(it >> 32), (uint32_t)it, true);
+      }
+    }, k, nwords, S);
+  } else {
+    exact_select([&](auto fn) { for_each_key(sc, n, fn); }, k, nwords, S);
+  }
 
   // 3. The chosen rows in ascending order.
   const int per = (nwords + kSelThreads - 1) / kSelThreads;

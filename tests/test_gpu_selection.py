@@ -119,3 +119,27 @@ def test_built_selection_feeds_sparse_attention(da):
         assert np.array_equal(sel.cpu().numpy(), ref_sel)
         H.check_tolerance(H.from_dev(out), oracle.sparse(q, k, v, ref_sel, case.scale),
                           f"replay {it}")
+
+
+@pytest.mark.parametrize("k_idx,case", [(3000, "sample misleads"), (1500, "sample agrees"),
+                                        (4000, "large k"), (1920, "nan and ties")])
+def test_prefiltered_and_fallback_paths(da, k_idx, case):
+    # The builder first keeps the keys at or above a bound taken from a sample
+    # of 256 runs of 8 keys; when fewer than k keys are kept it selects over all
+    # keys instead. Giving every sampled key a huge score with k above the
+    # sample size keeps only the sample (fewer than k) and forces that path;
+    # with k below the sample size the kept keys are exactly the sample.
+    B, n, W_, topk = 2, 65408, 0, 4096
+    s = scores_for(90 + k_idx, B, n)
+    if case in ("sample misleads", "sample agrees"):
+        for j in range(256):
+            start = (j * (n - 8) // 255) & ~3
+            s[:, start:start + 8] = 1.0e6 + j
+    elif case == "nan and ties":
+        s = np.round(s * 8) / 8
+        s[:, 5::301] = np.nan
+        s[:, 7::211] = -np.nan
+    pos = [-1] * B
+    got = run_builder(da, s, pos, n, k_idx, W_, 0, topk)
+    want = build_selection(s, pos, n, k_idx, W_, 0, topk)
+    assert np.array_equal(got, want), case
