@@ -1,35 +1,41 @@
-// kernels.hip -- split-K decode attention kernels for gfx950 (CDNA4).
+// kernels.hip -- decode attention kernels for gfx950 (CDNA4).
 //
-// The operation is softmax(scale * q . K^T) V for one query token per sequence
-// (fuel-dispatch page "DecodeFlashSpec": q [B, Hq, 1, D] against the capacity
-// buffers [B, Hkv, capacity, D] over the live prefix [0, k_len), grouped-query
-// heads), and its index-selected form (metrale page "AttnV41",
+// The operation is softmax(scale * q . K^T) V for the query tokens of each
+// sequence (fuel-dispatch page "DecodeFlashSpec": q [B, Hq, Sq, D] against the
+// capacity buffers [B, Hkv, capacity, D] over the live prefix [0, k_len),
+// grouped-query heads; Sq = 1 in decode, up to 16 with a causal mask over the
+// last Sq positions), and its index-selected form (metrale page "AttnV41",
 // decode_fixed_topk: rows named by a -1-padded selection; pads contribute
 // nothing).
 //
-// Decomposition (split-K over keys): one workgroup owns a (batch, kv head,
-// head tile, split); each of its four waves streams every fourth 32-key tile
-// of the split and keeps its own base-2 online-softmax state; the waves are
-// merged at the end, and a second kernel merges the splits (log-sum-exp).
+// Decompositions. attend_partial (split-K): one workgroup owns a (batch, kv
+// head, head tile, split). attend_balanced (one live length per sequence):
+// workgroup w owns an equal run of 32-key tiles of all (sequence, kv head,
+// head tile) key streams laid end to end. Either way the workgroup calls
+// attend_range on a key range, whose four waves each stream every fourth
+// 32-key tile and keep their own base-2 online-softmax state, merged at the
+// end; combine_splits / combine_balanced merge the partials (log-sum-exp).
 //
-// Per 32-key tile, for the (up to 16) query heads of the head tile:
-//   S^T[32 keys x 16 heads] = K_tile . Q^T  two v_mfma_f32_16x16x32_bf16 chains over D.
+// Per 32-key tile, for the (up to 16) query rows (heads x tokens) of the tile:
+//   S^T[32 keys x 16 rows] = K_tile . Q^T  two v_mfma_f32_16x16x32_bf16 chains over D.
 //       K is loaded from HBM straight into the A-operand layout: lane l holds
 //       16 bytes of key row (l % 16); a wave instruction reads 64 contiguous
 //       bytes of each of 16 rows, and the D/64 instructions cover the rows.
-//   softmax: scores * scale * log2(e); per-head running max m (wave-reduced),
+//   softmax: scores * scale * log2(e); per-row running max m (wave-reduced),
 //       weights p = 2^(s - m) rounded to bf16 (the same rounded weights feed the
 //       denominator l and the output), rescale of l and O by 2^(m_old - m_new).
-//   O^T[D x 16 heads] += V_tile^T . P^T   D/16 MFMAs, one per 16-wide d tile.
+//   O^T[D x 16 rows] += V_tile^T . P^T   D/16 MFMAs, one per 16-wide d tile.
 //       V is staged through LDS (coalesced 1 KiB-per-instruction loads, XOR-
 //       swizzled 16-byte chunks) and read back transposed with
 //       ds_read_b64_tr_b16, which hands each lane 4 keys of one d column.
 // The next tile's K and V loads are issued before the current tile is
 // processed (register double buffering), so every wave keeps 16 KiB in flight.
 //
-// Keys outside the split, past k_len, or (sparse) pads and out-of-range
-// entries are never loaded: their K and V rows are zeros and their score is
-// -inf, so their weight is exactly 0. A tile with no valid key is skipped.
+// Keys outside the range, past k_len, hidden by the causal mask, or (sparse)
+// pads and out-of-range entries get score -inf, so their weight is exactly 0;
+// a slot without a valid key reads an allowed row (never one at or past k_len)
+// and its V row is zeroed in LDS before use. A tile with no valid key is
+// skipped.
 #include "device_common.h"
 #include "launch.h"
 
