@@ -119,12 +119,24 @@ def build_inputs(args, torch, W, H):
     return case, host, 2 * k.nbytes, desc, cfg, case.algorithmic_bytes()
 
 
-def cpu_baseline(args, case, host, algo_bytes, W):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, case, host, algo_bytes, W, threads=None, seconds=None):
     """Time the fp64 oracle (as it stands) on this host over a bounded sample."""
     import numpy as np
 
     import oracle
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
+    seconds = args.cpu_seconds if seconds is None else seconds
     rows_total = case.B * case.Hq
     ragged = "lens" in host
     # About one second of all-core work per probe; grow the sample to ~10 s of wall.
@@ -158,16 +170,16 @@ def cpu_baseline(args, case, host, algo_bytes, W):
             oracle.sparse(host["q"], host["k"], host["v"], host["sel"], case.scale, case.rows,
                           rows=rows, threads=threads)
         t_probe = time.perf_counter() - t0
-        if t_probe >= args.cpu_seconds or n >= rows_total * 64:
+        if t_probe >= seconds or n >= (1 << 24):
             break
-        grow = max(2.0, min(8.0, args.cpu_seconds / max(t_probe, 1e-3)))
+        grow = max(2.0, min(8.0, seconds / max(t_probe, 1e-3)))
         n = int(n * grow)
         if ragged:
             n = case.B * -(-n // case.B)
     per_step = t_probe * rows_total / n
     return {
         "value": round(algo_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model(),
         "sample": (f"{n} query rows (b, h) of the {rows_total} in one step"
                    f"{' (rows repeated)' if n > rows_total else ''}, {t_probe:.2f} s wall on "
                    f"{threads} threads, scaled to a full step ({per_step * 1e3:.1f} ms/step)"),
@@ -289,6 +301,8 @@ def main():
                     help="dense: each step is one decode_attn_dense_step call, which writes the "
                          "pass's new K/V rows at the end of each prefix and attends (one kernel "
                          "pair instead of append + attention)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement (a 4 GiB read probe)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -421,6 +435,17 @@ def main():
 
     kern_ms = np.array([ev_b[i].elapsed_time(ev_a[i]) for i in range(args.steps)])
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Warm: workloads rotated over several K/V copies (to defeat the 256 MB
+    # Infinity Cache) are also timed on one copy, the cache-resident case.
+    warm_us = None
+    if sets > 1:
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            step(0)
+        torch.cuda.synchronize()
+        warm_us = (time.perf_counter() - w0) * 1e6 / args.steps
     value = algo_bytes / (ms_per_step * 1e-3) / 1e9
     kern_mean_s = float(kern_ms.mean()) * 1e-3
     achieved = algo_bytes / kern_mean_s / 1e9
@@ -465,6 +490,25 @@ def main():
         log(f"graph replay: {graph_us:.1f} us/step")
         del graph
 
+    # The measured streaming-read ceiling: a plain read of 4 GiB with the same
+    # load style, timed with events on the current stream.
+    ceiling = None
+    if not args.no_ceiling:
+        buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            da.decode_attn_read_probe(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            da.decode_attn_read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ceiling = buf.numel() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        log(f"streaming-read ceiling: {ceiling:.0f} GB/s")
+        del buf, sink
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -500,20 +544,28 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
+            "frac_of_measured_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
             "traffic": traffic,
             "kernel": ("attend_balanced (length-balanced stream of K and V)" if ragged or one_call
                        else "attend_partial (split-K stream of K and V)"),
             "kernel_us_mean": round(kern_mean_s * 1e6, 3),
+            "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
             "bytes_per_launch": algo_bytes,
         },
         "cpu_baseline": None,
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
+        "warm_us_per_step": None if warm_us is None else round(warm_us, 3),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(args, case, host, algo_bytes, W)
+        if args.workload in ("tiny", "sparse"):
+            one = cpu_baseline(args, case, host, algo_bytes, W, threads=1,
+                               seconds=args.cpu_seconds / 2)
+            result["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "sample")}
     print(json.dumps(result), flush=True)
 
 

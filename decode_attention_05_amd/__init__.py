@@ -22,7 +22,8 @@ __all__ = [
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_dense_ragged",
     "decode_attn_dense_paged", "decode_attn_dense_step", "decode_attn_sparse",
     "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
-    "decode_attn_set_timing_events", "decode_attn_status_str", "decode_attn_last_error",
+    "decode_attn_set_timing_events", "decode_attn_read_probe", "decode_attn_status_str",
+    "decode_attn_last_error",
     "workspace_for",
     "EXPORTED_SYMBOLS",
 ]
@@ -34,6 +35,7 @@ DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = ra
 
 EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
                     "decode_attn_dense_ragged", "decode_attn_dense_paged", "decode_attn_dense_step",
+                    "decode_attn_read_probe",
                     "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
@@ -124,6 +126,8 @@ def library():
                                                ctypes.c_int32, P, ctypes.c_float, P,
                                                ctypes.c_size_t, P]
         lib.decode_attn_dense_step.restype = ctypes.c_int
+        lib.decode_attn_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+        lib.decode_attn_read_probe.restype = ctypes.c_int
         lib.decode_attn_sparse.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_int32, P,
                                            ctypes.c_float, ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_sparse.restype = ctypes.c_int
@@ -146,6 +150,19 @@ def _status_name(s: int) -> str:
         return library().decode_attn_status_str(s).decode()
     except Exception:  # pragma: no cover - only while reporting another error
         return f"status {s}"
+
+
+def decode_attn_read_probe(buf, sink, stream=None):
+    """Read all of ``buf`` (a contiguous device tensor, a multiple of 16 bytes) the
+    way the attention kernels stream K and V, folding it into ``sink`` (a
+    one-element int32 device tensor): the measured streaming-read ceiling."""
+    import torch
+    if not (isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous()):
+        raise TypeError("buf must be a contiguous device tensor")
+    _tensor_ptr(sink, "sink", (1,), torch.int32)
+    _check(library().decode_attn_read_probe(ctypes.c_void_p(buf.data_ptr()),
+                                            buf.numel() * buf.element_size(),
+                                            ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
 
 
 def decode_attn_set_timing_events(ev_before, ev_after):

@@ -24,6 +24,7 @@
 
 #include "append.h"
 #include "launch.h"
+#include "probe.h"
 #include "select.h"
 
 namespace {
@@ -618,6 +619,22 @@ decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, vo
   const hipError_t e = da::launch_append(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(DA_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+decode_attn_status decode_attn_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                                         void* stream) {
+  if (!buf || !sink) return fail(DA_ERR_INVALID_ARG, "buf and sink must be non-NULL");
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u))
+    return fail(DA_ERR_INVALID_ARG, "buf must be 16-byte and sink 4-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(DA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  int cus = 0;
+  decode_attn_status s = device_cus(&cus);
+  if (s != DA_OK) return s;
+  const hipError_t e =
+      da::launch_read_probe(buf, (int64_t)bytes, sink, cus, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -325,6 +325,19 @@ decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, vo
  */
 decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after);
 
+/*
+ * Diagnostics: the measured streaming-read ceiling. Reads `bytes` (a positive
+ * multiple of 16) of device memory at `buf` (16-byte aligned) with the
+ * attention kernels' load style (16-byte non-temporal loads, two workgroups
+ * per compute unit, each reading a contiguous share) and XORs a fold of every
+ * word into *sink (device, 4-byte aligned), so the reads cannot be dropped.
+ * Time it with events on `stream` to get the achievable read bandwidth the
+ * attention kernels are compared with. Returns DA_OK, DA_ERR_INVALID_ARG or
+ * DA_ERR_HIP. (Not part of the operation; for benchmarks.)
+ */
+decode_attn_status decode_attn_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                                          void* stream);
+
 /* Static string naming a status code. */
 const char* decode_attn_status_str(decode_attn_status s);
 

@@ -316,3 +316,13 @@ def test_ragged_and_paged_fail_closed(da):
                                  G.workspace_bytes, None) == 1
     assert lib.decode_attn_dense_devlen(ctypes.byref(G), fake, fake, fake, fake, 0.1, fake, ws,
                                         G.workspace_bytes, None) == 1
+
+
+def test_read_probe_fails_closed(da):
+    lib = da.library()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.decode_attn_read_probe(None, 1024, fake, None) == 1
+    assert lib.decode_attn_read_probe(fake, 1024, None, None) == 1
+    assert lib.decode_attn_read_probe(ctypes.c_void_p(0x10004), 1024, fake, None) == 1
+    assert lib.decode_attn_read_probe(fake, 1000, fake, None) == 1
+    assert lib.decode_attn_read_probe(fake, 0, fake, None) == 1
