@@ -394,22 +394,31 @@ def main():
         dtable = None
         splits = plan.balanced_wgs
 
-    def step(i):
-        kk, vv = dks[i % sets], dvs[i % sets]
+    # Each K/V set's step, checked and marshalled once (PreparedCall): the timed
+    # loop then only enqueues.
+    def calls_for(kk, vv):
         if one_call:
-            da.decode_attn_dense_step(plan, dq, kk, vv, kn, vn, dlens, out, case.scale,
-                                      block_table=dtable if paged else None, workspace=ws)
-        elif paged:
-            da.decode_attn_dense_paged(plan, dq, kk, vv, dtable, dlens, out, case.scale,
-                                       workspace=ws)
-        elif ragged:
-            da.decode_attn_dense_ragged(plan, dq, kk, vv, out, case.scale, dlens, workspace=ws)
-        elif sparse:
-            da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows, ws)
-        else:
-            if append:
-                da.decode_attn_append_kv(kk, vv, kn, vn, pos_dev)
-            da.decode_attn_dense(plan, dq, kk, vv, out, case.scale, case.k_len, ws)
+            return [da.decode_attn_dense_step(plan, dq, kk, vv, kn, vn, dlens, out, case.scale,
+                                              block_table=dtable if paged else None,
+                                              workspace=ws, prepare=True)]
+        if paged:
+            return [da.decode_attn_dense_paged(plan, dq, kk, vv, dtable, dlens, out, case.scale,
+                                               workspace=ws, prepare=True)]
+        if ragged:
+            return [da.decode_attn_dense_ragged(plan, dq, kk, vv, out, case.scale, dlens,
+                                                workspace=ws, prepare=True)]
+        if sparse:
+            return [da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale,
+                                          case.rows, ws, prepare=True)]
+        seq = [da.decode_attn_append_kv(kk, vv, kn, vn, pos_dev, prepare=True)] if append else []
+        return seq + [da.decode_attn_dense(plan, dq, kk, vv, out, case.scale, case.k_len, ws,
+                                           prepare=True)]
+
+    prepared = [calls_for(dks[i], dvs[i]) for i in range(sets)]
+
+    def step(i):
+        for call in prepared[i % sets]:
+            call()
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -461,9 +470,11 @@ def main():
                               device="cuda")
 
         def gstep(i):
+            # direct calls: they take torch's current stream, the capturing one
             kk, vv = dks[i % sets], dvs[i % sets]
             if ragged or one_call:
-                step(i)
+                for call in calls_for(kk, vv):  # prepared here, on the current stream
+                    call()
             elif sparse:
                 da.decode_attn_sparse(plan, dq, kk, vv, dsel, case.topk, out, case.scale, case.rows,
                                       ws)

@@ -25,7 +25,7 @@ __all__ = [
     "decode_attn_set_timing_events", "decode_attn_read_probe", "decode_attn_status_str",
     "decode_attn_last_error",
     "workspace_for",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "PreparedCall",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -183,6 +183,33 @@ def _check(status: int):
         raise DecodeAttnError(status, decode_attn_last_error())
 
 
+class PreparedCall:
+    """One library call with its arguments checked and marshalled once (the
+    ``prepare=True`` form of every compute wrapper). Calling it enqueues the
+    same call again on the same buffers and on the stream chosen when it was
+    prepared (by default torch's current stream at that moment), without
+    re-checking shapes in Python; it keeps the plan, the problem struct and the
+    tensors alive."""
+
+    __slots__ = ("_fn", "_args", "_keep", "_result")
+
+    def __init__(self, fn, args, keep, result):
+        self._fn, self._args, self._keep, self._result = fn, args, keep, result
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != DA_OK:
+            raise DecodeAttnError(status, decode_attn_last_error())
+        return self._result
+
+
+def _run(fn, args, result, prepare, keep):
+    if prepare:
+        return PreparedCall(fn, tuple(args), keep, result)
+    _check(fn(*args))
+    return result
+
+
 def decode_attn_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                      capacity: int, max_k_len: int | None = None, *, topk_max: int = 0,
                      kv_batch: int = 0, seq_q: int = 1, causal: bool = False,
@@ -242,8 +269,9 @@ def _stream_ptr(stream):
 
 
 def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int,
-                      workspace=None, stream=None):
-    """Enqueue dense decode attention on ``stream`` (default: torch's current stream)."""
+                      workspace=None, stream=None, prepare=False):
+    """Enqueue dense decode attention on ``stream`` (default: torch's current stream).
+    With ``prepare=True`` return a PreparedCall instead of calling."""
     import torch
     p = plan.prob
     B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
@@ -252,13 +280,13 @@ def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int
     args = (_tensor_ptr(q, "q", (B, Hq, Sq, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
             _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_dense(ctypes.byref(plan), *args, float(softmax_scale), int(k_len),
-                                       ws, wsb, _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_dense,
+                (ctypes.byref(plan), *args, float(softmax_scale), int(k_len), ws, wsb,
+                 _stream_ptr(stream)), out, prepare, (plan, q, k, v, out, workspace))
 
 
 def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_len_dev,
-                             workspace=None, stream=None):
+                             workspace=None, stream=None, prepare=False):
     """Dense decode attention whose live length is the int32 in ``k_len_dev`` (a
     one-element device tensor), read by the kernel: capturable once, replayable."""
     import torch
@@ -270,9 +298,9 @@ def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_l
             _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     klen = _tensor_ptr(k_len_dev, "k_len_dev", (1,), torch.int32)
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_dense_devlen(ctypes.byref(plan), *args, float(softmax_scale),
-                                              klen, ws, wsb, _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_dense_devlen,
+                (ctypes.byref(plan), *args, float(softmax_scale), klen, ws, wsb,
+                 _stream_ptr(stream)), out, prepare, (plan, q, k, v, out, k_len_dev, workspace))
 
 
 def _lens_ptr(k_lens, B, stride):
@@ -286,7 +314,8 @@ def _lens_ptr(k_lens, B, stride):
 
 
 def decode_attn_dense_ragged(plan: Plan, q, k, v, out, softmax_scale: float, k_lens,
-                             k_lens_stride: int = 1, workspace=None, stream=None):
+                             k_lens_stride: int = 1, workspace=None, stream=None,
+                             prepare=False):
     """Dense decode attention with sequence b's length k_lens[b * k_lens_stride] (device)."""
     import torch
     p = plan.prob
@@ -297,15 +326,14 @@ def decode_attn_dense_ragged(plan: Plan, q, k, v, out, softmax_scale: float, k_l
             _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
     lens = _lens_ptr(k_lens, B, k_lens_stride)
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_dense_ragged(ctypes.byref(plan), *args, float(softmax_scale),
-                                              lens, int(k_lens_stride), ws, wsb,
-                                              _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_dense_ragged,
+                (ctypes.byref(plan), *args, float(softmax_scale), lens, int(k_lens_stride), ws,
+                 wsb, _stream_ptr(stream)), out, prepare, (plan, q, k, v, out, k_lens, workspace))
 
 
 def decode_attn_dense_paged(plan: Plan, q, k_pages, v_pages, block_table, k_lens, out,
                             softmax_scale: float, k_lens_stride: int = 1, workspace=None,
-                            stream=None):
+                            stream=None, prepare=False):
     """Dense decode attention over page pools [num_pages,Hkv,page_size,D] through
     block_table [B, max_pages_per_seq] (int32, device)."""
     import torch
@@ -320,15 +348,15 @@ def decode_attn_dense_paged(plan: Plan, q, k_pages, v_pages, block_table, k_lens
     lens = _lens_ptr(k_lens, B, k_lens_stride)
     op = _tensor_ptr(out, "out", (B, Hq, Sq, D), bf)
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_dense_paged(ctypes.byref(plan), qp, kp, vp, bt, lens,
-                                             int(k_lens_stride), op, float(softmax_scale), ws, wsb,
-                                             _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_dense_paged,
+                (ctypes.byref(plan), qp, kp, vp, bt, lens, int(k_lens_stride), op,
+                 float(softmax_scale), ws, wsb, _stream_ptr(stream)), out, prepare,
+                (plan, q, k_pages, v_pages, block_table, k_lens, out, workspace))
 
 
 def decode_attn_dense_step(plan: Plan, q, k_cache, v_cache, k_new, v_new, k_lens, out,
                            softmax_scale: float, block_table=None, k_lens_stride: int = 1,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, prepare=False):
     """Write the pass's new K/V rows [B, Hkv, Sq, D] at rows [k_len - Sq, k_len) of
     each sequence's cache and attend, in one call (contiguous caches with a
     ragged plan, or page pools with a paged plan and ``block_table``)."""
@@ -352,14 +380,14 @@ def decode_attn_dense_step(plan: Plan, q, k_cache, v_cache, k_new, v_new, k_lens
     lens = _lens_ptr(k_lens, B, k_lens_stride)
     op = _tensor_ptr(out, "out", (B, Hq, Sq, D), bf)
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_dense_step(ctypes.byref(plan), qp, kc, vc, kn, vn, bt, lens,
-                                            int(k_lens_stride), op, float(softmax_scale), ws, wsb,
-                                            _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_dense_step,
+                (ctypes.byref(plan), qp, kc, vc, kn, vn, bt, lens, int(k_lens_stride), op,
+                 float(softmax_scale), ws, wsb, _stream_ptr(stream)), out, prepare,
+                (plan, q, k_cache, v_cache, k_new, v_new, block_table, k_lens, out, workspace))
 
 
 def decode_attn_sparse(plan: Plan, q, k, v, sel, topk: int, out, softmax_scale: float,
-                       k_len: int | None = None, workspace=None, stream=None):
+                       k_len: int | None = None, workspace=None, stream=None, prepare=False):
     """Enqueue index-selected sparse decode attention (sel: int32 [B, topk])."""
     import torch
     p = plan.prob
@@ -371,14 +399,14 @@ def decode_attn_sparse(plan: Plan, q, k, v, sel, topk: int, out, softmax_scale: 
             _tensor_ptr(sel, "sel", (B, topk), torch.int32))
     outp = _tensor_ptr(out, "out", (B, Hq, 1, D), bf)
     ws, wsb = _ws_ptr(plan, workspace)
-    _check(library().decode_attn_sparse(ctypes.byref(plan), *args, int(topk), outp,
-                                        float(softmax_scale), int(cap if k_len is None else k_len),
-                                        ws, wsb, _stream_ptr(stream)))
-    return out
+    return _run(library().decode_attn_sparse,
+                (ctypes.byref(plan), *args, int(topk), outp, float(softmax_scale),
+                 int(cap if k_len is None else k_len), ws, wsb, _stream_ptr(stream)), out,
+                prepare, (plan, q, k, v, sel, out, workspace))
 
 
 def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window: int,
-                                win_base: int, stream=None):
+                                win_base: int, stream=None, prepare=False):
     """Fill ``sel`` [B, topk] int32 on the device: window ring rows, then the k_idx
     best-scoring candidates of ``scores`` [B, >= n_idx] fp32, then -1 (``pos`` [B] int32)."""
     import torch
@@ -389,13 +417,13 @@ def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window
     sp = _tensor_ptr(scores, "scores", (B, stride), torch.float32)
     pp = _tensor_ptr(pos, "pos", (B,), torch.int32)
     selp = _tensor_ptr(sel, "sel", (B, topk), torch.int32)
-    _check(library().decode_attn_build_selection(ctypes.byref(prob), sp, pp, selp,
-                                                 _stream_ptr(stream)))
-    return sel
+    return _run(library().decode_attn_build_selection,
+                (ctypes.byref(prob), sp, pp, selp, _stream_ptr(stream)), sel, prepare,
+                (prob, scores, pos, sel))
 
 
 def decode_attn_append_kv(k_cache, v_cache, k_new, v_new, pos, window: int = 0, win_base: int = 0,
-                          stream=None):
+                          stream=None, prepare=False):
     """Write token b's rows k_new/v_new [B,Hkv,1,D] into the caches [B,Hkv,capacity,D] at
     row pos[b] (or win_base + pos[b] % window); ``pos`` is an int32 device tensor [B]."""
     import torch
@@ -407,5 +435,5 @@ def decode_attn_append_kv(k_cache, v_cache, k_new, v_new, pos, window: int = 0, 
             _tensor_ptr(k_new, "k_new", (B, Hkv, 1, D), bf),
             _tensor_ptr(v_new, "v_new", (B, Hkv, 1, D), bf),
             _tensor_ptr(pos, "pos", (B,), torch.int32))
-    _check(library().decode_attn_append_kv(ctypes.byref(prob), *args, _stream_ptr(stream)))
-    return k_cache, v_cache
+    return _run(library().decode_attn_append_kv, (ctypes.byref(prob), *args, _stream_ptr(stream)),
+                (k_cache, v_cache), prepare, (prob, k_cache, v_cache, k_new, v_new, pos))

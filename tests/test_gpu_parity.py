@@ -261,3 +261,23 @@ def test_binding_rejects_mismatched_tensors(da):
         da.decode_attn_dense(plan, q, kv, kv, out, 0.1, 50, da.workspace_for(plan))
     with pytest.raises(TypeError):
         da.decode_attn_dense(plan, q.float(), kv, kv, out, 0.1, 50, da.workspace_for(plan))
+
+
+def test_prepared_call_matches_the_direct_call(da):
+    # The prepare=True form checks and marshals once; each call enqueues again.
+    import torch
+    q, k, v = W.random_case(61, 2, 16, 4, 128, 3000)
+    plan = da.decode_attn_plan(2, 16, 4, 128, 3000, 3000)
+    dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+    ws = da.workspace_for(plan)
+    a = torch.empty((2, 16, 1, 128), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    H.log("prepared dense call")
+    call = da.decode_attn_dense(plan, dq, dk, dv, a, 0.1, 2500, ws, prepare=True)
+    assert isinstance(call, da.PreparedCall)
+    da.decode_attn_dense(plan, dq, dk, dv, b, 0.1, 2500, ws)
+    for _ in range(3):
+        a.fill_(float("nan"))
+        assert call() is a
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
