@@ -143,3 +143,42 @@ def test_prefiltered_and_fallback_paths(da, k_idx, case):
     got = run_builder(da, s, pos, n, k_idx, W_, 0, topk)
     want = build_selection(s, pos, n, k_idx, W_, 0, topk)
     assert np.array_equal(got, want), case
+
+
+N_RANDOM = 16
+
+
+def draw_selection_case(i):
+    rng = np.random.Generator(np.random.PCG64(500 + i))
+    B = int(rng.integers(1, 5))
+    n = int(rng.choice([1, 7, 100, 4095, 8191, 8192, 20000, 65408, 131072]))
+    k = int(rng.choice([0, 1, 17, 640, 1920, 4096]))
+    window = int(rng.choice([0, 1, 64, 128]))
+    topk = int(rng.integers(max(1, window), window + min(k, n) + 64))
+    kind = ["normal", "uniform", "ties", "special", "trend", "constant"][i % 6]
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    if kind == "uniform":
+        s = rng.uniform(-1, 1, (B, n)).astype(np.float32)
+    elif kind == "ties":
+        s = np.round(s * 4) / 4
+    elif kind == "special":
+        s[:, ::53] = np.inf
+        s[:, 3::61] = -np.inf
+        s[:, 5::67] = np.nan
+        s[:, 7::71] = -0.0
+    elif kind == "trend":
+        s = (np.arange(n, dtype=np.float32) / n + 0.01 * s).astype(np.float32)
+    elif kind == "constant":
+        s[:] = 0.5
+    pos = [int(x) for x in rng.integers(-1, 2 * max(1, window) + 5, size=B)]
+    return dict(B=B, n=n, k=k, window=window, topk=topk, kind=kind, pos=pos), s
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
+def test_random_selections(da, i):
+    c, s = draw_selection_case(i)
+    win_base = c["n"]
+    H.log(f"random selection {i}: {c}")
+    got = run_builder(da, s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"])
+    want = build_selection(s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"])
+    assert np.array_equal(got, want), c
