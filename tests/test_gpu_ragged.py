@@ -300,3 +300,30 @@ def test_full_size_sampled(da, name):
         heads = rng.choice(case.Hq, 4, replace=False)
         ref = oracle.dense(q[b:b + 1], kb, vb, case.scale, int(lens[b]), rows=heads)
         H.check_tolerance(got[b, heads, 0], ref, f"{name} b={b} heads={heads.tolist()}")
+
+
+@pytest.mark.parametrize("B,num_cus,Sq", [(200, 0, 1), (130, 7, 3), (1000, 0, 1)])
+def test_many_sequences(da, B, num_cus, Sq):
+    # more than 64 sequences: the schedule reads the lengths in several
+    # 64-sequence chunks (totals, the prefix scan that locates a run's first
+    # stream, the combine's stream offsets)
+    import torch
+    Hq, Hkv, D, cap = 4, 2, 64, 600
+    rng = np.random.Generator(np.random.PCG64(400 + B))
+    lens = [int(x) for x in rng.integers(0, cap + 1, size=B)]
+    lens[::17] = [0] * len(lens[::17])
+    sq, sk, sv, _ = W.seeds(401 + B)
+    q = W.normal_bf16(sq, (B, Hq, Sq, D))
+    k = W.normal_bf16(sk, (B, Hkv, cap, D))
+    v = W.normal_bf16(sv, (B, Hkv, cap, D))
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, seq_q=Sq, causal=True, ragged=True,
+                               num_cus=num_cus)
+    out = torch.full((B, Hq, Sq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    H.log(f"ragged many sequences B={B} Sq={Sq} wgs={plan.balanced_wgs}")
+    da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.1,
+                                H.to_dev_i32(lens), workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    got = H.from_dev(out)
+    ref = oracle.dense_ragged(q, k, v, 0.1, lens, True)
+    H.check_tolerance(got, ref, f"B={B}")
+    assert not got[~ref.any(axis=-1)].any()
