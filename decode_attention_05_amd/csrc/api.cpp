@@ -84,24 +84,28 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // --- split-K heuristic -------------------------------------------------------
 //
 // The hot path is bound by HBM bandwidth, so the grid must keep every CU
-// streaming, in one round of equally sized workgroups: the attention kernel
-// keeps kResidentPerCu workgroups resident per CU (2 waves/SIMD, 4 waves per
-// workgroup), and a grid that is not a whole number of workgroups per CU leaves
-// CUs idle at the end (measured: 384 or 640 workgroups on 256 CUs run 15-20%
-// slower than 256 or 512). A unit (batch, kv head, head tile) is split only when
-// there are fewer units than CUs, into at most kResidentPerCu * CUs / units
-// splits, and never below kMinChunk keys (kMinSparseChunk selection entries) per
-// split: below that the split merge costs more than the streaming it spreads.
+// streaming, in one round of equally sized workgroups. Each CU's read rate is
+// close to its own limit when it holds one 4-wave workgroup, so a CU given more
+// workgroups than another finishes last (measured: 288 workgroups on 256 CUs run
+// 57% slower than 256), and two per CU contend for HBM without reading faster
+// (512 workgroups of half the keys run 2-3% slower than 256). A unit (batch, kv
+// head, head tile) is split only when there are fewer units than CUs, into
+// CUs / units splits (rounded down: a CU left idle costs less than a CU given
+// two), and never below kMinChunk keys per split: below that the split merge
+// costs more than the streaming it spreads. The selection gather is bound by
+// latency instead, so sparse chunks are sized for kResidentPerCu workgroups per
+// CU, and never below kMinSparseChunk selection entries.
 constexpr int kResidentPerCu = 2;
 constexpr int kMinChunk = 1024;
 constexpr int kMinSparseChunk = 128;
 constexpr int kKeyAlign = 32;  // the kernel's key tile: splits start on tile (and page) edges
 constexpr int kMaxSplits = 1 << 16;
 
-// Splits per unit that fill the resident slots once (1 when units >= CUs).
-int64_t splits_for_occupancy(int64_t units, int cus) {
+// Splits per unit that give every CU at most per_cu workgroups in one round
+// (1 when units >= CUs).
+int64_t splits_for_occupancy(int64_t units, int cus, int per_cu) {
   if (units >= cus) return 1;
-  return std::max<int64_t>(1, (int64_t)kResidentPerCu * cus / units);
+  return std::max<int64_t>(1, (int64_t)per_cu * cus / units);
 }
 
 // Query heads per workgroup: the largest divisor of G whose rows (heads times
@@ -126,7 +130,7 @@ void dense_split(const decode_attn_plan_t& P, int64_t k_len, int* S_out, int* ch
     S = ceil_div(k_len, chunk);
     bound = S;
   } else {
-    int64_t target = p.force_splits > 0 ? p.force_splits : splits_for_occupancy(units, P.num_cus);
+    int64_t target = p.force_splits > 0 ? p.force_splits : splits_for_occupancy(units, P.num_cus, 1);
     const int64_t min_chunk = p.force_splits > 0 ? 1 : kMinChunk;
     int64_t s0 = std::min<int64_t>(target, ceil_div(k_len, min_chunk));
     s0 = std::max<int64_t>(1, std::min<int64_t>(s0, kMaxSplits));
@@ -403,7 +407,7 @@ decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_pl
     if (p->force_chunk > 0) {
       chunk = p->force_chunk;
     } else {
-      const int64_t per_unit = splits_for_occupancy(units, cus);
+      const int64_t per_unit = splits_for_occupancy(units, cus, kResidentPerCu);
       chunk = round_up(ceil_div(p->topk_max, per_unit), kKeyAlign);
       chunk = std::max<int64_t>(chunk, std::min<int64_t>(kMinSparseChunk, round_up(p->topk_max, kKeyAlign)));
     }

@@ -129,21 +129,23 @@ def test_invalid_problems(da, kw):
 
 def test_dense_plans_for_the_workloads(da):
     # With 256 compute units: split only when there are fewer (batch, kv head)
-    # units than CUs, fill 2 resident workgroups per CU once, keep >= 1024 keys
-    # per split.
+    # units than CUs, give each CU one workgroup, keep >= 1024 keys per split.
     tiny = da.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256)
     assert tiny.num_splits_max == 1 and tiny.workspace_bytes == 0
     gqa = da.decode_attn_plan(8, 32, 8, 128, 8192, 4096, num_cus=256)
     assert gqa.num_splits_max == 4 and gqa.chunk == 1024
     assert gqa.workspace_bytes == 8 * 32 * 4 * 130 * 4
     long = da.decode_attn_plan(4, 64, 8, 128, 131072, 131072, num_cus=256)
-    assert long.num_splits_max == 16 and long.chunk == 8192
-    assert long.workspace_bytes == 4 * 64 * 16 * 130 * 4
+    assert long.num_splits_max == 8 and long.chunk == 16384
+    assert long.workspace_bytes == 4 * 64 * 8 * 130 * 4
+    # 48 units: 5 splits (240 workgroups), not 6 (288: 32 CUs would get two)
+    six = da.decode_attn_plan(6, 64, 8, 128, 65536, 65536, num_cus=256)
+    assert six.num_splits_max == 5
     batch = da.decode_attn_plan(128, 32, 8, 128, 2048, 1537, num_cus=256)
     assert batch.num_splits_max == 1 and batch.workspace_bytes == 0
     # query heads beyond 16 per kv head are served by several head tiles
     wide = da.decode_attn_plan(4, 64, 1, 128, 8192, 8192, num_cus=256)
-    assert wide.group == 64 and wide.num_splits_max == 8  # 16 units -> 32 splits, capped at 8192/1024
+    assert wide.group == 64 and wide.num_splits_max == 8  # 16 units -> 16 splits, capped at 8192/1024
 
 
 def test_sparse_plan_chunk_is_independent_of_call(da):
