@@ -288,6 +288,9 @@ def main():
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
                              "paged", "verify", "select", "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--events-every", type=int, default=8,
+                    help="bracket the streaming kernel with HIP events on every Nth timed "
+                         "step (an event pair adds ~6 us to the step it is in)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing of the plan-once call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -426,23 +429,28 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    every = max(1, args.events_every)
+    timed = list(range(0, args.steps, every))   # timed steps whose kernel is bracketed
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in timed]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in timed]
     for e in ev_b + ev_a:      # create the underlying hipEvent_t before handing it over
         e.record(stream)
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps (kernel events on every {every}th)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        da.decode_attn_set_timing_events(ev_b[i].cuda_event, ev_a[i].cuda_event)
+        if i % every == 0:
+            da.decode_attn_set_timing_events(ev_b[i // every].cuda_event, ev_a[i // every].cuda_event)
+        elif i % every == 1:
+            da.decode_attn_set_timing_events(None, None)
         step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     da.decode_attn_set_timing_events(None, None)
 
-    kern_ms = np.array([ev_b[i].elapsed_time(ev_a[i]) for i in range(args.steps)])
+    kern_ms = np.array([ev_b[j].elapsed_time(ev_a[j]) for j in range(len(timed))])
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # Warm: workloads rotated over several K/V copies (to defeat the 256 MB
@@ -564,6 +572,7 @@ def main():
             "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
+            "kernel_launches_timed": len(kern_ms),
             "bytes_per_launch": algo_bytes,
         },
         "cpu_baseline": None,
