@@ -420,6 +420,8 @@ decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_pl
   P.workspace_bytes = workspace_for(P.prob, P.num_splits_max);
   if (P.kind == 0 && (p->ragged || p->page_size > 0)) {
     P.prob.ragged = 1;
+    // Two workgroups per CU: the schedule's piece boundaries leave bubbles in
+    // one workgroup's stream that the other fills (measured faster than one).
     P.balanced_wgs = kResidentPerCu * cus;
     P.workspace_bytes = std::max(P.workspace_bytes, balanced_workspace(P));
   }
