@@ -223,18 +223,22 @@ def bench_selection(args, torch, np, da, W, H):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    every = max(1, args.events_every)
+    timed = list(range(0, args.steps, every))   # timed steps whose builder launch is bracketed
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in timed]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in timed]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev_b[i].record(stream)
+        if i % every == 0:
+            ev_b[i // every].record(stream)
         da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
-        ev_a[i].record(stream)
+        if i % every == 0:
+            ev_a[i // every].record(stream)
         if built:
             da.decode_attn_sparse(plan, dq, dk, dv, dsel, case.topk, out, case.scale, case.rows, ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = np.array([ev_b[i].elapsed_time(ev_a[i]) for i in range(args.steps)])
+    kern_ms = np.array([ev_b[j].elapsed_time(ev_a[j]) for j in range(len(timed))])
     us = (t1 - t0) * 1e6 / args.steps
     kern_us = float(kern_ms.mean()) * 1e3
     log(f"{us:.1f} us/step, selection kernel mean {kern_us:.1f} us")
@@ -273,7 +277,8 @@ def bench_selection(args, torch, np, da, W, H):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(sel_bytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
                      "traffic": None, "kernel": "selection builder",
-                     "kernel_us_mean": round(kern_us, 3), "bytes_per_launch": sel_bytes},
+                     "kernel_us_mean": round(kern_us, 3), "kernel_launches_timed": len(kern_ms),
+                     "bytes_per_launch": sel_bytes},
         "cpu_baseline": cpu,
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
     }), flush=True)

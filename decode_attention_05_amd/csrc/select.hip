@@ -63,7 +63,8 @@ constexpr int kPreMinN = 8192;             // rows below this go straight to the
 // IEEE 754 totalOrder as an unsigned key: larger float -> larger key.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: every bit flipped; otherwise the sign bit set (shift, or, xor)
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Sort item: ascending order = (score desc, index asc).
