@@ -302,6 +302,36 @@ def test_full_size_sampled(da, name):
         H.check_tolerance(got[b, heads, 0], ref, f"{name} b={b} heads={heads.tolist()}")
 
 
+@pytest.mark.parametrize("B,num_cus,Sq,ties", [(64, 0, 1, False), (64, 5, 2, True),
+                                                (63, 0, 1, True), (65, 0, 1, True)])
+def test_length_order_boundaries(da, B, num_cus, Sq, ties):
+    # up to 64 sequences are laid shortest first (ties in index order), ranked
+    # in one wave: 64 uses every lane, 65 falls back to index order. Lengths
+    # with many ties, zeros and the extremes.
+    import torch
+    Hq, Hkv, D, cap = 8, 2, 64, 700
+    rng = np.random.Generator(np.random.PCG64(450 + B + int(ties)))
+    pool = [0, 1, 31, 32, 33, 300, cap] if ties else None
+    lens = ([int(x) for x in rng.choice(pool, size=B)] if ties
+            else [int(x) for x in rng.integers(0, cap + 1, size=B)])
+    lens[B // 2] = cap
+    sq, sk, sv, _ = W.seeds(451 + B)
+    q = W.normal_bf16(sq, (B, Hq, Sq, D))
+    k = W.normal_bf16(sk, (B, Hkv, cap, D))
+    v = W.normal_bf16(sv, (B, Hkv, cap, D))
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, seq_q=Sq, causal=True, ragged=True,
+                               num_cus=num_cus)
+    out = torch.full((B, Hq, Sq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    H.log(f"length order B={B} Sq={Sq} ties={ties} wgs={plan.balanced_wgs}")
+    da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.1,
+                                H.to_dev_i32(lens), workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    got = H.from_dev(out)
+    ref = oracle.dense_ragged(q, k, v, 0.1, lens, True)
+    H.check_tolerance(got, ref, f"B={B}")
+    assert not got[~ref.any(axis=-1)].any()
+
+
 @pytest.mark.parametrize("B,num_cus,Sq", [(200, 0, 1), (130, 7, 3), (1000, 0, 1)])
 def test_many_sequences(da, B, num_cus, Sq):
     # more than 64 sequences: the schedule reads the lengths in several
