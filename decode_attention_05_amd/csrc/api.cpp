@@ -244,10 +244,11 @@ uint64_t workspace_for(const decode_attn_problem& p, int S) {
 }
 
 // Length-balanced schedule: two partial slots of (heads per workgroup) x
-// (tokens) rows per workgroup.
+// (tokens) rows per run, and up to one run per wave (4 per workgroup).
+constexpr int kWavesPerWg = 4;
 uint64_t balanced_workspace(const decode_attn_plan_t& P) {
-  return (uint64_t)P.balanced_wgs * 2 * heads_per_wg(P.group, P.prob.seq_q) * P.prob.seq_q *
-         (P.prob.head_dim + 2) * sizeof(float);
+  return (uint64_t)P.balanced_wgs * kWavesPerWg * 2 * heads_per_wg(P.group, P.prob.seq_q) *
+         P.prob.seq_q * (P.prob.head_dim + 2) * sizeof(float);
 }
 
 decode_attn_status check_common(const decode_attn_plan_t* plan, int kind, const void* q,
@@ -319,7 +320,7 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
   L.k_lens_stride = k_lens_stride;
   L.sparse = false;
   L.balanced_wgs = plan->balanced_wgs;
-  const int64_t slots = (int64_t)plan->balanced_wgs * 2 * L.heads_per_wg * L.Sq;
+  const int64_t slots = (int64_t)plan->balanced_wgs * kWavesPerWg * 2 * L.heads_per_wg * L.Sq;
   float* ws = static_cast<float*>(workspace);
   L.part_o = ws;
   L.part_m = ws + slots * plan->prob.head_dim;

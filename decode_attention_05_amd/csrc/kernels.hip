@@ -126,7 +126,7 @@ struct RangeOut {
 // k_len - Sq + 1 + t. Every thread of the workgroup must call it with the same
 // arguments; it synchronises the workgroup and uses all of `lds`, so a caller
 // that calls it again first synchronises.
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool WAVE = false>
 __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned char* lds,
                                              float (&mrg_m)[kWaves][16],
                                              float (&mrg_l)[kWaves][16], int b, int hkv,
@@ -352,26 +352,55 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
-  // Wave `wave` takes tiles wave, wave + 4, ...; the next tile's loads are in
-  // flight while the current one is processed.
+  // Wave `wave` takes tiles wave, wave + 4, ... (a wave-local range: every
+  // tile); the next tile's loads are in flight while the current one is
+  // processed.
+  constexpr int kStep = WAVE ? 1 : kWaves;
   {
     TileRegs<D> A, B;
-    int tau = wave;
+    int tau = WAVE ? 0 : wave;
     load_tile(A, tau);
     while (tau < ntiles) {
-      load_tile(B, tau + kWaves);
+      load_tile(B, tau + kStep);
       process_tile(A);
-      tau += kWaves;
+      tau += kStep;
       if (tau >= ntiles) break;
-      load_tile(A, tau + kWaves);
+      load_tile(A, tau + kStep);
       process_tile(B);
-      tau += kWaves;
+      tau += kStep;
     }
   }
 
   // Denominator of head r16 over the four lane groups.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+
+  if constexpr (WAVE) {
+    // One wave owns the range: lane (g, r16) holds values 16 dt + 4 g .. + 3
+    // of row r16 and writes them itself, with no merge and no barrier.
+    if (r16 < RT) {
+      if (ro.direct) {
+        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        uint16_t* dst = ro.out + (int64_t)r16 * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<uint2*>(dst + 16 * dt) =
+              make_uint2(pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
+                         pack_bf16(O[dt][2] * inv, O[dt][3] * inv));
+      } else {
+        float* po = ro.po + r16 * ro.po_stride + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<float4*>(po + 16 * dt) =
+              make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
+        if (g == 0) {
+          ro.pm[r16 * ro.pm_stride] = m;
+          ro.pl[r16 * ro.pm_stride] = l;
+        }
+      }
+    }
+    return;
+  }
 
   __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
   float* mo = reinterpret_cast<float*>(lds);
@@ -491,14 +520,14 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
 // 32-key tiles, laid end to end sequence by sequence (shortest first for up to
 // 64 sequences, see length_order; index order beyond), then kv head, then head
 // tile.
-// Workgroup w takes tiles [w * per_wg, (w + 1) * per_wg) of that concatenation,
-// so every workgroup streams the same number of tiles whatever the mix of
-// lengths. A stream that lies inside one workgroup's run is finished there
-// (bf16 output); a stream cut by a run boundary leaves one fp32 partial per
-// workgroup that touches it, in slot 0 of the workgroup (the first stream of
-// its run) or slot 1 (the last), and the combine merges them. Both kernels
-// derive the schedule from the lengths alone, with the same integer
-// arithmetic.
+// Run w (a workgroup, or a wave when streams are many, see wave_runs) takes
+// tiles [w * per_run, (w + 1) * per_run) of that concatenation, so every run
+// streams the same number of tiles whatever the mix of lengths. A stream that
+// lies inside one run is finished there (bf16 output); a stream cut by a run
+// boundary leaves one fp32 partial per run that touches it, in slot 0 of the
+// run (the first stream of the run) or slot 1 (the last), and the combine
+// merges them. Both kernels derive the schedule from the lengths alone, with
+// the same integer arithmetic.
 
 constexpr int64_t kMinTilesPerWg = 8;
 
@@ -524,18 +553,55 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Tiles per workgroup run for `total` tiles over all streams.
-__device__ __forceinline__ int64_t run_tiles(const PartialLaunch& a, int64_t total) {
-  const int64_t even = (total + a.balanced_wgs - 1) / a.balanced_wgs;
+// Tiles per run for `total` tiles over all streams cut into `runs` runs.
+__device__ __forceinline__ int64_t run_tiles(int64_t total, int64_t runs) {
+  const int64_t even = (total + runs - 1) / runs;
   return even > kMinTilesPerWg ? even : kMinTilesPerWg;
 }
 
-// Tiles over all streams, sequences in index order (more than 64 sequences).
-__device__ __forceinline__ int64_t total_tiles(const PartialLaunch& a, int streams_per_seq) {
+// Runs: one per workgroup, or one per wave when there are at least as many
+// non-empty streams as waves. With many short streams a workgroup's run cuts
+// through several of them, and every piece costs the four waves a pipeline
+// fill and a merge behind a barrier; one wave per run streams its pieces alone,
+// writes its own rows, and its bubbles are filled by the CU's other waves
+// (measured on 512 sequences of 128 to 2048 keys, 8 kv heads: 4,775 GB/s with a
+// run per workgroup, 5,492 GB/s with a run per wave).
+__device__ __forceinline__ bool wave_runs(const PartialLaunch& a, int64_t nonempty_seqs,
+                                          int streams_per_seq) {
+  return nonempty_seqs * streams_per_seq >= (int64_t)a.balanced_wgs * kWaves;
+}
+
+// More than 64 sequences are read kLenGroup at a time, kLenGroup / 64 per
+// lane (sequence base + 64 i + lane in slot i), all loads issued before any is
+// used; 0 past the batch.
+constexpr int kLenSlots = 8;
+constexpr int kLenGroup = 64 * kLenSlots;
+
+__device__ __forceinline__ void load_lengths(const PartialLaunch& a, int base,
+                                             int (&len)[kLenSlots]) {
   const int lane = threadIdx.x & 63;
-  int64_t mine = 0;
-  for (int base = 0; base < a.B; base += 64)
-    if (base + lane < a.B) mine += tiles_of(seq_len(a, base + lane));
+#pragma unroll
+  for (int i = 0; i < kLenSlots; ++i) {
+    const int bb = base + 64 * i + lane;
+    len[i] = bb < a.B ? (int)seq_len(a, bb) : 0;
+  }
+}
+
+// Tiles over all streams and the number of non-empty sequences, sequences in
+// index order (more than 64 sequences).
+__device__ __forceinline__ int64_t total_tiles(const PartialLaunch& a, int streams_per_seq,
+                                               int64_t* nonempty) {
+  int64_t mine = 0, live = 0;
+  for (int base = 0; base < a.B; base += kLenGroup) {
+    int len[kLenSlots];
+    load_lengths(a, base, len);
+#pragma unroll
+    for (int i = 0; i < kLenSlots; ++i) {
+      mine += tiles_of(len[i]);
+      live += len[i] > 0 ? 1 : 0;
+    }
+  }
+  *nonempty = uniform_i64(wave_sum_i64(live));
   return uniform_i64(wave_sum_i64(mine)) * streams_per_seq;
 }
 
@@ -577,31 +643,21 @@ __device__ __forceinline__ SeqOrder length_order(const PartialLaunch& a, int str
   return o;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) {
-  using Gm = Geometry<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
-  __shared__ float mrg_m[kWaves][16];
-  __shared__ float mrg_l[kWaves][16];
-
+// The pieces of run `run` of `runs` (per_run tiles each): the whole workgroup
+// (WAVE false) or one wave (WAVE true) walks them.
+template <int D, bool WAVE>
+__device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char* lds,
+                                           float (&mrg_m)[kWaves][16],
+                                           float (&mrg_l)[kWaves][16], int64_t run,
+                                           int64_t per_run, int64_t total, int per_seq,
+                                           bool by_length, const SeqOrder& o) {
   const int lane = threadIdx.x & 63;
   const int GT = a.heads_per_wg;
   const int RT = GT * a.Sq;             // query rows of one stream
   const int tiles_h = a.G / GT;
-  const int per_seq = a.Hkv * tiles_h;  // streams per sequence
-  const bool by_length = a.B <= 64;
-  SeqOrder o{};
-  int64_t total;
-  if (by_length) {
-    o = length_order(a, per_seq);
-    total = o.total;
-  } else {
-    total = total_tiles(a, per_seq);
-  }
-  const int64_t per_wg = run_tiles(a, total);
-  const int64_t t0 = (int64_t)blockIdx.x * per_wg;
-  if (t0 >= total) return;  // the whole workgroup leaves together
-  const int64_t t1 = (t0 + per_wg < total) ? t0 + per_wg : total;
+  const int64_t t0 = run * per_run;
+  if (t0 >= total) return;  // the whole workgroup (or wave) leaves together
+  const int64_t t1 = (t0 + per_run < total) ? t0 + per_run : total;
 
   // The sequence whose streams hold tile t0.
   int b = 0;
@@ -615,25 +671,32 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
   } else {
     // Index order: the first b with per_seq * (tiles before b) <= t0 <
     // per_seq * (tiles up to b), 64 sequences per step, lane-parallel scan.
-    int64_t run = 0;
-    for (int base = 0; base < a.B; base += 64) {
-      const int64_t n = (base + lane < a.B) ? tiles_of(seq_len(a, base + lane)) * per_seq : 0;
-      int64_t inc = n;
+    int64_t acc = 0;
+    bool found = false;
+    for (int base = 0; base < a.B && !found; base += kLenGroup) {
+      int len[kLenSlots];
+      load_lengths(a, base, len);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int64_t y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
+      for (int i = 0; i < kLenSlots; ++i) {
+        if (found) break;
+        const int64_t n = tiles_of(len[i]) * per_seq;
+        int64_t inc = n;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int64_t y = __shfl_up(inc, off);
+          if (lane >= off) inc += y;
+        }
+        inc += acc;
+        const int64_t exc = inc - n;
+        const uint64_t hit = __ballot(n > 0 && exc <= t0 && t0 < inc);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          b = base + 64 * i + src;
+          seq_start = uniform_i64(__shfl(exc, src));
+          found = true;
+        }
+        acc = uniform_i64(__shfl(inc, 63));
       }
-      inc += run;
-      const int64_t exc = inc - n;
-      const uint64_t hit = __ballot(n > 0 && exc <= t0 && t0 < inc);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        b = base + src;
-        seq_start = uniform_i64(__shfl(exc, src));
-        break;
-      }
-      run = uniform_i64(__shfl(inc, 63));
     }
   }
   b = __builtin_amdgcn_readfirstlane(b);
@@ -656,18 +719,19 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
     RangeOut ro;
     ro.direct = (jt == 0 && nt == nb);  // the whole stream is in this run
     ro.out = a.out + row0 * D;
-    const int64_t slot = ((int64_t)blockIdx.x * 2 + (x == t0 ? 0 : 1)) * RT;
+    const int64_t slot = (run * 2 + (x == t0 ? 0 : 1)) * RT;
     ro.po = a.part_o + slot * D;
     ro.pm = a.part_m + slot;
     ro.pl = a.part_l + slot;
     ro.po_stride = D;
     ro.pm_stride = 1;
     const int64_t j1 = (jt + nt) * kTileKeys;
-    attend_range<D, false>(a, lds, mrg_m, mrg_l, b, hkv, row0, RT, len, jt * kTileKeys,
-                           j1 < len ? j1 : len, ro);
+    attend_range<D, false, WAVE>(a, lds, mrg_m, mrg_l, b, hkv, row0, RT, len, jt * kTileKeys,
+                                 j1 < len ? j1 : len, ro);
     x += nt;
     if (x >= t1) break;
-    __syncthreads();  // the merge area is read before the next range's V tiles land there
+    // the merge area is read before the next range's V tiles land there
+    if constexpr (!WAVE) __syncthreads();
     // Next stream: the next head tile / kv head, else the next non-empty sequence.
     jt = 0;
     if (++r == per_seq) {
@@ -680,6 +744,40 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
       } while (nb == 0);
       if (b >= a.B) break;  // unreachable: tiles remain before t1 <= total
     }
+  }
+}
+
+// MAY_WAVE: the batch has enough streams for one run per wave to be possible
+// (decided on the host from the shapes; the lengths decide on the device). A
+// batch that cannot qualify gets a kernel without the per-wave path, whose
+// registers the workgroup path then has to itself.
+template <int D, bool MAY_WAVE>
+__global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) {
+  using Gm = Geometry<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
+  __shared__ float mrg_m[kWaves][16];
+  __shared__ float mrg_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  const int per_seq = a.Hkv * (a.G / a.heads_per_wg);  // streams per sequence
+  const bool by_length = a.B <= 64;
+  SeqOrder o{};
+  int64_t total, nonempty;
+  if (by_length) {
+    o = length_order(a, per_seq);
+    total = o.total;
+    nonempty = __builtin_popcountll(__ballot(lane < a.B && o.len > 0));
+  } else {
+    total = total_tiles(a, per_seq, &nonempty);
+  }
+  if (MAY_WAVE && wave_runs(a, nonempty, per_seq)) {
+    const int64_t runs = (int64_t)a.balanced_wgs * kWaves;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    run_pieces<D, true>(a, lds, mrg_m, mrg_l, (int64_t)blockIdx.x * kWaves + wave,
+                        run_tiles(total, runs), total, per_seq, by_length, o);
+  } else {
+    run_pieces<D, false>(a, lds, mrg_m, mrg_l, (int64_t)blockIdx.x,
+                         run_tiles(total, a.balanced_wgs), total, per_seq, by_length, o);
   }
 }
 
@@ -704,7 +802,7 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
 
   // The schedule of attend_balanced: every tile, and the tiles laid before
   // sequence b's streams (shortest first up to 64 sequences, else index order).
-  int64_t total, before_b;
+  int64_t total, before_b, nonempty;
   if (a.B <= 64) {
     // the sequences laid before b: shorter ones, and equal ones of lower index
     const int len = lane < a.B ? (int)seq_len(a, lane) : 0;
@@ -712,18 +810,27 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
     const bool earlier = lane < a.B && (len < len_b || (len == len_b && lane < b));
     total = uniform_i64(wave_sum_i64(lane < a.B ? tiles_of(len) : 0)) * per_seq;
     before_b = uniform_i64(wave_sum_i64(earlier ? tiles_of(len) : 0)) * per_seq;
+    nonempty = __builtin_popcountll(__ballot(lane < a.B && len > 0));
   } else {
-    int64_t all = 0, before = 0;
-    for (int base = 0; base < a.B; base += 64) {
-      const int bb = base + lane;
-      const int64_t n = bb < a.B ? tiles_of(seq_len(a, bb)) : 0;
-      all += n;
-      before += bb < b ? n : 0;
+    int64_t all = 0, before = 0, live = 0;
+    for (int base = 0; base < a.B; base += kLenGroup) {
+      int len[kLenSlots];
+      load_lengths(a, base, len);
+#pragma unroll
+      for (int i = 0; i < kLenSlots; ++i) {
+        const int64_t n = tiles_of(len[i]);
+        all += n;
+        before += base + 64 * i + lane < b ? n : 0;
+        live += n > 0 ? 1 : 0;
+      }
     }
     total = uniform_i64(wave_sum_i64(all)) * per_seq;
     before_b = uniform_i64(wave_sum_i64(before)) * per_seq;
+    nonempty = uniform_i64(wave_sum_i64(live));
   }
-  const int64_t per_wg = run_tiles(a, total);
+  const int64_t runs = wave_runs(a, nonempty, per_seq) ? (int64_t)a.balanced_wgs * kWaves
+                                                      : (int64_t)a.balanced_wgs;
+  const int64_t per_run = run_tiles(total, runs);
   const int64_t nb = tiles_of(seq_len(a, b));
   if (nb == 0) {
     if (hh < RT) {
@@ -735,11 +842,11 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
     return;
   }
   const int64_t ts = before_b + (int64_t)r * nb;
-  const int64_t ws = ts / per_wg, we = (ts + nb - 1) / per_wg;
+  const int64_t ws = ts / per_run, we = (ts + nb - 1) / per_run;
   if (ws == we || hh >= RT) return;
 
   auto slot_of = [&](int64_t w) -> int64_t {
-    const int first = (w > ws || ts == w * per_wg) ? 0 : 1;
+    const int first = (w > ws || ts == w * per_run) ? 0 : 1;
     return (w * 2 + first) * RT + hh;
   };
   // M over the pieces: the 16 threads of a head take every 16th piece.
@@ -868,8 +975,13 @@ hipError_t launch_partial_d(const PartialLaunch& L, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_balanced_d(const PartialLaunch& L, hipStream_t stream) {
-  hipLaunchKernelGGL(attend_balanced<D>, dim3((unsigned)L.balanced_wgs), dim3(kThreads), 0, stream,
-                     L);
+  const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
+  if (streams >= (int64_t)L.balanced_wgs * kWaves)
+    hipLaunchKernelGGL((attend_balanced<D, true>), dim3((unsigned)L.balanced_wgs), dim3(kThreads),
+                       0, stream, L);
+  else
+    hipLaunchKernelGGL((attend_balanced<D, false>), dim3((unsigned)L.balanced_wgs),
+                       dim3(kThreads), 0, stream, L);
   return hipGetLastError();
 }
 

@@ -23,9 +23,10 @@ struct PartialLaunch {
   int64_t num_pages;
   uint16_t* out;       // [B, Hq, Sq, D] bf16: written directly when S == 1
   float* part_o;       // [B*Hq*Sq, S, D] fp32 unnormalised partial outputs (S > 1); balanced
-                       // schedule: [balanced_wgs, 2, heads_per_wg, D]
-  float* part_m;       // [B*Hq*Sq, S] running max, base 2 (S > 1); balanced: [balanced_wgs, 2,
-                       // heads_per_wg]
+                       // schedule: [runs, 2, heads_per_wg * Sq, D] with up to
+                       // 4 * balanced_wgs runs
+  float* part_m;       // [B*Hq*Sq, S] running max, base 2 (S > 1); balanced: [runs, 2,
+                       // heads_per_wg * Sq]
   float* part_l;       // [B*Hq*Sq, S] softmax denominators (S > 1); balanced: as part_m
   int balanced_wgs;    // workgroups of the length-balanced schedule (ragged calls)
   int B, Hq, Hkv, G, D;

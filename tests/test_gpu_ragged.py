@@ -332,6 +332,79 @@ def test_length_order_boundaries(da, B, num_cus, Sq, ties):
     assert not got[~ref.any(axis=-1)].any()
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,num_cus,Sq,paged", [
+    (512, 16, 8, 64, 0, 1, False),    # ~3950 streams: one run per wave on 256 CUs
+    (520, 16, 8, 64, 0, 1, True),     # paged, beyond 512 sequences (two length groups)
+    (40, 16, 4, 128, 4, 4, False),    # shortest-first order with wave runs, 4 tokens
+    (24, 32, 8, 128, 2, 1, True),     # head tiles of 4 heads, paged
+])
+def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
+    # at least as many non-empty streams as waves: every wave walks its own run
+    # and writes its own rows or partials, with no workgroup merge
+    import torch
+    cap, page = 640, 64
+    rng = np.random.Generator(np.random.PCG64(470 + B))
+    lens = [int(x) for x in np.exp(rng.uniform(np.log(20), np.log(cap), size=B))]
+    lens[::29] = [0] * len(lens[::29])
+    lens[1] = cap
+    sq, sk, sv, _ = W.seeds(471 + B)
+    q = W.normal_bf16(sq, (B, Hq, Sq, D))
+    kw = dict(seq_q=Sq, causal=True, num_cus=num_cus)
+    if paged:
+        max_pages = cap // page
+        table, num_pages = W.page_table(rng, lens, page, max_pages, 2)
+        k = W.normal_bf16(sk, (num_pages, Hkv, page, D))
+        v = W.normal_bf16(sv, (num_pages, Hkv, page, D))
+        plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, page_size=page,
+                                   max_pages_per_seq=max_pages, num_pages=num_pages, **kw)
+    else:
+        k = W.normal_bf16(sk, (B, Hkv, cap, D))
+        v = W.normal_bf16(sv, (B, Hkv, cap, D))
+        plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True, **kw)
+    G = Hq // Hkv
+    gt = max(d for d in range(1, 16 // Sq + 1) if G % d == 0)   # query heads per stream
+    streams = sum(1 for n in lens if n > 0) * Hkv * (G // gt)
+    assert streams >= plan.balanced_wgs * 4
+    out = torch.full((B, Hq, Sq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    H.log(f"wave runs B={B} Hq={Hq} Hkv={Hkv} D={D} Sq={Sq} paged={paged} wgs={plan.balanced_wgs}")
+    ws = da.workspace_for(plan)
+    if paged:
+        da.decode_attn_dense_paged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev_i32(table),
+                                   H.to_dev_i32(lens), out, 0.1, workspace=ws)
+    else:
+        da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.1,
+                                    H.to_dev_i32(lens), workspace=ws)
+    torch.cuda.synchronize()
+    got = H.from_dev(out)
+    ref = (oracle.dense_paged(q, k, v, table, 0.1, lens, True) if paged
+           else oracle.dense_ragged(q, k, v, 0.1, lens, True))
+    H.check_tolerance(got, ref, f"wave runs B={B}")
+    assert not got[~ref.any(axis=-1)].any()
+
+
+def test_few_live_streams_in_a_wide_batch(da):
+    # 512 sequences x 8 kv heads could give one run per wave, but only 90 are
+    # non-empty (720 streams): the per-workgroup runs of the same kernel
+    import torch
+    B, Hq, Hkv, D, cap = 512, 16, 8, 64, 300
+    rng = np.random.Generator(np.random.PCG64(480))
+    lens = [0] * B
+    for b in rng.choice(B, size=90, replace=False):
+        lens[int(b)] = int(rng.integers(1, cap + 1))
+    sq, sk, sv, _ = W.seeds(481)
+    q = W.normal_bf16(sq, (B, Hq, 1, D))
+    k = W.normal_bf16(sk, (B, Hkv, cap, D))
+    v = W.normal_bf16(sv, (B, Hkv, cap, D))
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
+    assert 90 * Hkv < plan.balanced_wgs * 4 <= B * Hkv
+    out = _out(B, Hq, D)
+    H.log("wide batch, few live streams")
+    da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.1,
+                                H.to_dev_i32(lens), workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    _check_ragged(H.from_dev(out), q, k, v, 0.1, lens, "few live streams")
+
+
 @pytest.mark.parametrize("B,num_cus,Sq", [(200, 0, 1), (130, 7, 3), (1000, 0, 1)])
 def test_many_sequences(da, B, num_cus, Sq):
     # more than 64 sequences: the schedule reads the lengths in several

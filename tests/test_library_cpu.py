@@ -263,16 +263,16 @@ def test_paged_plans(da):
 
 
 def test_ragged_plans(da):
-    # the length-balanced schedule: two resident workgroups per CU, two partial
-    # slots of heads_per_wg rows each
+    # the length-balanced schedule: two resident workgroups per CU, up to one
+    # run per wave (4 per workgroup), two partial slots of heads_per_wg rows per run
     dense = plan(da)
     R = plan(da, ragged=True)
     assert dense.balanced_wgs == 0 and R.balanced_wgs == 512 and R.prob.ragged == 1
     assert (R.num_splits_max, R.chunk) == (dense.num_splits_max, dense.chunk)
-    assert R.workspace_bytes == max(dense.workspace_bytes, 512 * 2 * 8 * 130 * 4)
+    assert R.workspace_bytes == max(dense.workspace_bytes, 512 * 4 * 2 * 8 * 130 * 4)
     assert paged_plan(da).balanced_wgs == 512  # paged plans are always ragged
     tiny = da.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256, ragged=True)
-    assert tiny.workspace_bytes == 512 * 2 * 1 * 66 * 4
+    assert tiny.workspace_bytes == 512 * 4 * 2 * 1 * 66 * 4
     with pytest.raises(da.DecodeAttnError) as ei:
         da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=64, kv_batch=1, num_cus=256,
                             ragged=True)
