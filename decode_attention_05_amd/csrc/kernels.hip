@@ -782,7 +782,8 @@ __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) 
 }
 
 // Merge of the partials of one stream (b, kv head, head tile) cut by the
-// balanced schedule; one workgroup per stream, thread t owns head t / 16 and
+// balanced schedule; one workgroup per stream (16 threads per row: 64, 128 or
+// 256 threads), thread t owns row t / 16 of the stream and
 // D/16 values. Streams inside one run were finished by attend_balanced and are
 // left alone; an empty sequence gets zeros. Partials are merged in run order
 // with weights 2^(m - M).
@@ -988,7 +989,10 @@ hipError_t launch_balanced_d(const PartialLaunch& L, hipStream_t stream) {
 template <int D>
 hipError_t launch_balanced_combine_d(const PartialLaunch& L, hipStream_t stream) {
   const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
-  hipLaunchKernelGGL(combine_balanced<D>, dim3((unsigned)streams), dim3(256), 0, stream, L);
+  // 16 threads per row of the stream, whole waves: 64 threads for up to 4 rows
+  const int rows = L.heads_per_wg * L.Sq;
+  const int threads = rows <= 4 ? 64 : (rows <= 8 ? 128 : 256);
+  hipLaunchKernelGGL(combine_balanced<D>, dim3((unsigned)streams), dim3(threads), 0, stream, L);
   return hipGetLastError();
 }
 
