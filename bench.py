@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
-                             "paged", "verify", "select", "sparse_built"])
+                             "paged", "verify", "wide", "select", "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events-every", type=int, default=8,
                     help="bracket the streaming kernel with HIP events on every Nth timed "

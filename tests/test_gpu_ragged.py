@@ -264,7 +264,7 @@ def test_paged_graph_replay_follows_lengths_and_table(da):
                           f"replay {it}")
 
 
-@pytest.mark.parametrize("name", ["ragged", "paged"])
+@pytest.mark.parametrize("name", ["ragged", "paged", "wide"])
 def test_full_size_sampled(da, name):
     # the benchmark's own workload and launch, checked on sampled sequences and heads
     import torch

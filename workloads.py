@@ -28,6 +28,9 @@ follows the metrale page "AttnV41", decode_fixed_topk and decode_prep):
 * ``paged``    the same lengths over a paged cache of 64-row pages, shuffled
 * ``verify``   the ``ragged`` batch with 4 query tokens per sequence (causal: the
                last 4 positions of each live prefix), as in verifying drafted tokens
+* ``wide``     B=512 Hq=32 Hkv=8 D=128, one live length per sequence: 2048 for
+               sequence 0, log-uniform in [128, 2048] for the rest (a wide serving
+               batch: more key streams than the GPU has waves)
 """
 
 from __future__ import annotations
@@ -273,6 +276,8 @@ RAGGED_CASES = {
                         page_size=64, seed=6),
     "verify": RaggedCase("verify", 32, 32, 8, 128, 512, 32768, _f32(1.0 / math.sqrt(128)),
                          seq_q=4, seed=6),
+    # a wide serving batch: 512 sequences of 128..2048 keys (4,096 streams)
+    "wide": RaggedCase("wide", 512, 32, 8, 128, 128, 2048, _f32(1.0 / math.sqrt(128)), seed=7),
 }
 
 
