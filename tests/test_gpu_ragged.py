@@ -337,6 +337,8 @@ def test_length_order_boundaries(da, B, num_cus, Sq, ties):
     (520, 16, 8, 64, 0, 1, True),     # paged, beyond 512 sequences (two length groups)
     (40, 16, 4, 128, 4, 4, False),    # shortest-first order with wave runs, 4 tokens
     (24, 32, 8, 128, 2, 1, True),     # head tiles of 4 heads, paged
+    (12, 16, 4, 64, 3, 16, False),    # 16 tokens: one head per stream, 16 rows, D = 64
+    (30, 64, 1, 128, 2, 2, True),     # 64 heads on one kv head: 8 head tiles, paged
 ])
 def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
     # at least as many non-empty streams as waves: every wave walks its own run
