@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
 // merges them. Both kernels derive the schedule from the lengths alone, with
 // the same integer arithmetic.
 
-constexpr int64_t kMinTilesPerWg = 8;
+constexpr int64_t kMinTilesPerRun = 8;
 
 __device__ __forceinline__ int64_t seq_len(const PartialLaunch& a, int b) {
   const int64_t raw = a.k_len_dev[(int64_t)b * a.k_lens_stride];
@@ -556,7 +556,7 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
 // Tiles per run for `total` tiles over all streams cut into `runs` runs.
 __device__ __forceinline__ int64_t run_tiles(int64_t total, int64_t runs) {
   const int64_t even = (total + runs - 1) / runs;
-  return even > kMinTilesPerWg ? even : kMinTilesPerWg;
+  return even > kMinTilesPerRun ? even : kMinTilesPerRun;
 }
 
 // Runs: one per workgroup, or one per wave when there are at least as many
@@ -565,7 +565,7 @@ __device__ __forceinline__ int64_t run_tiles(int64_t total, int64_t runs) {
 // fill and a merge behind a barrier; one wave per run streams its pieces alone,
 // writes its own rows, and its bubbles are filled by the CU's other waves
 // (measured on 512 sequences of 128 to 2048 keys, 8 kv heads: 4,775 GB/s with a
-// run per workgroup, 5,492 GB/s with a run per wave).
+// run per workgroup, 5,651 GB/s with a run per wave, merge included).
 __device__ __forceinline__ bool wave_runs(const PartialLaunch& a, int64_t nonempty_seqs,
                                           int streams_per_seq) {
   return nonempty_seqs * streams_per_seq >= (int64_t)a.balanced_wgs * kWaves;
@@ -643,8 +643,9 @@ __device__ __forceinline__ SeqOrder length_order(const PartialLaunch& a, int str
   return o;
 }
 
-// The pieces of run `run` of `runs` (per_run tiles each): the whole workgroup
-// (WAVE false) or one wave (WAVE true) walks them.
+// The pieces of run `run` (tiles [run * per_run, (run + 1) * per_run) of the
+// concatenation): the whole workgroup (WAVE false) or one wave (WAVE true)
+// walks them.
 template <int D, bool WAVE>
 __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char* lds,
                                            float (&mrg_m)[kWaves][16],
