@@ -328,8 +328,9 @@ decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after
 /*
  * Diagnostics: the measured streaming-read ceiling. Reads `bytes` (a positive
  * multiple of 16) of device memory at `buf` (16-byte aligned) with the
- * attention kernels' load style (16-byte non-temporal loads, two workgroups
- * per compute unit, each reading a contiguous share) and XORs a fold of every
+ * attention kernels' load style (16-byte non-temporal loads, one workgroup
+ * per compute unit, each reading a contiguous share with sixteen loads in
+ * flight per thread, the fastest shape measured) and XORs a fold of every
  * word into *sink (device, 4-byte aligned), so the reads cannot be dropped.
  * Time it with events on `stream` to get the achievable read bandwidth the
  * attention kernels are compared with. Returns DA_OK, DA_ERR_INVALID_ARG or

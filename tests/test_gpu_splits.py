@@ -6,7 +6,9 @@ regrouping of the sums that define the attention output (fuel-dispatch page
 "DecodeFlashSpec", the decomposed reference arm), so every case is checked
 against the fp64 oracle. These tests check that plans can share one workspace,
 that many calls in flight on one stream agree bit for bit, the merge's looped
-path past 16 splits, and plans with thousands of units.
+path past 16 splits, and plans with thousands of units. The streaming-read
+probe the benchmark compares the kernels with is checked here too: it must
+read every word of its buffer.
 """
 
 import pytest
@@ -124,3 +126,20 @@ def test_thousands_of_split_units(da):
     H.check_tolerance(H.from_dev(out), oracle.dense(q, k, v, 0.125, 90), "4160 units")
 
 
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (1 << 20) + 48, (3 << 20) + 16 * 7])
+def test_read_probe_reads_every_word(da, nbytes):
+    # the streaming-read probe folds every 32-bit word into the sink with xor:
+    # whole steps and the share's tail alike (shares of 256 workgroups)
+    import numpy as np
+    import torch
+    rng = np.random.Generator(np.random.PCG64(760 + nbytes))
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H.log(f"read probe {nbytes} bytes")
+    da.decode_attn_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    expect = np.bitwise_xor.reduce(words) if words.size else np.uint32(0)
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(expect)
