@@ -1,6 +1,8 @@
 // api.cpp -- the C ABI of the decode-attention library: problem validation, the
-// split-K plan, and the two compute entry points. Host code only; the kernels
-// live in kernels.hip.
+// split-K plan, and the entry points (dense with a host, device or per-sequence
+// length, paged, the one-call pass, sparse, the selection builder, the KV
+// append, and diagnostics). Host code only; the kernels live in kernels.hip,
+// select.hip, append.hip and probe.hip.
 //
 // The problem statement follows the fuel-dispatch page "DecodeFlashSpec"
 // (shapes of q, k, v; softmax_scale; k_len as the live prefix, counting the
