@@ -67,6 +67,31 @@ def test_contiguous_step(da, B, Hq, Hkv, Sq, D, cap, lens, causal):
     assert not got[~ref.any(axis=-1)].any()
 
 
+def test_wide_step_with_wave_runs(da):
+    # the one-call pass on a batch wide enough for one run per wave
+    import torch
+    B, Hq, Hkv, Sq, D, cap = 64, 16, 8, 2, 64, 400
+    rng = np.random.Generator(np.random.PCG64(360))
+    lens = [int(x) for x in rng.integers(Sq, cap + 1, size=B)]
+    sq, sk, sv, _ = W.seeds(361)
+    q = W.normal_bf16(sq, (B, Hq, Sq, D))
+    k = W.normal_bf16(sk, (B, Hkv, cap, D))
+    v = W.normal_bf16(sv, (B, Hkv, cap, D))
+    kn, vn = _new_rows(362, B, Hkv, Sq, D)
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, seq_q=Sq, causal=True, ragged=True,
+                               num_cus=16)
+    assert B * Hkv >= plan.balanced_wgs * 4
+    dk, dv = H.to_dev(k), H.to_dev(v)
+    out = _out(B, Hq, Sq, D)
+    H.log(f"wide step B={B} wgs={plan.balanced_wgs}")
+    da.decode_attn_dense_step(plan, H.to_dev(q), dk, dv, H.to_dev(kn), H.to_dev(vn),
+                              H.to_dev_i32(lens), out, 0.1, workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    ka, va = append_rows(k, v, kn, vn, lens)
+    assert np.array_equal(H.from_dev(dk), ka) and np.array_equal(H.from_dev(dv), va)
+    H.check_tolerance(H.from_dev(out), oracle.dense_ragged(q, ka, va, 0.1, lens, True), "wide step")
+
+
 def test_step_equals_append_then_attend(da):
     # bit for bit: the same keys in the same order, one kernel fewer
     import torch
