@@ -890,15 +890,16 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
 // Log-sum-exp merge of the S split partials: one wave per output row, four rows
 // per workgroup, lane l owning D/64 output values. With at most kFastSplits
 // splits every load (the running maxima, denominators and partial outputs of
-// all splits; rows past the last split re-read it and get weight 0) is issued
-// before any is used, so the merge costs about one memory round trip; more
+// all splits, in NS register slots, the next power of two of S; slots past the
+// last split re-read it and get weight 0) is issued before any is used, so the
+// merge costs about one memory round trip; more
 // splits run the same arithmetic in a loop. M = max_s m_s, weights 2^(m_s - M)
 // (exactly 0 for an empty split, whose partial holds zeros), sums in split
 // order. With one non-empty split its weight is exactly 1 and every other term
 // an exact 0, so the result equals the one-split output bit for bit.
 constexpr int kFastSplits = 16;
 
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
   constexpr int PER = D / 64;  // outputs per lane
   const int lane = threadIdx.x & 63;
@@ -913,10 +914,10 @@ __global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
   float M = kNegInf, L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  if (S <= kFastSplits) {
-    float m[kFastSplits], l[kFastSplits], o[kFastSplits][PER];
+  if constexpr (NS > 0) {
+    float m[NS], l[NS], o[NS][PER];
 #pragma unroll
-    for (int s = 0; s < kFastSplits; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const int j = s < S ? s : S - 1;
       m[s] = pm[j];
       l[s] = pl[j];
@@ -929,13 +930,13 @@ __global__ __launch_bounds__(256) void combine_splits(PartialLaunch a) {
       }
     }
 #pragma unroll
-    for (int s = 0; s < kFastSplits; ++s) {
+    for (int s = 0; s < NS; ++s) {
       if (s >= S) m[s] = kNegInf;
       M = fmaxf(M, m[s]);
     }
     if (M != kNegInf) {
 #pragma unroll
-      for (int s = 0; s < kFastSplits; ++s) {
+      for (int s = 0; s < NS; ++s) {
         const float w = exp2_fast(m[s] - M);
         L += l[s] * w;
 #pragma unroll
@@ -1032,12 +1033,26 @@ hipError_t launch_combine(const PartialLaunch& L, hipStream_t stream) {
   const int64_t rows = (int64_t)L.B * L.Hq * L.Sq;
   if (rows <= 0 || rows > 0x7fffffff || L.S < 1) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)((rows + 3) / 4);  // one wave per row
-  if (L.D == 128)
-    hipLaunchKernelGGL(combine_splits<128>, dim3(grid), dim3(256), 0, stream, L);
-  else if (L.D == 64)
-    hipLaunchKernelGGL(combine_splits<64>, dim3(grid), dim3(256), 0, stream, L);
-  else
-    return hipErrorInvalidValue;
+  // The register-resident merge is sized to the next power of two of the split
+  // count (up to kFastSplits); more splits take the looped merge.
+  const int ns = L.S <= 2 ? 2 : (L.S <= 4 ? 4 : (L.S <= 8 ? 8 : (L.S <= kFastSplits ? 16 : 0)));
+#define DA_COMBINE(DD, NN) \
+  hipLaunchKernelGGL((combine_splits<DD, NN>), dim3(grid), dim3(256), 0, stream, L)
+  if (L.D != 128 && L.D != 64) return hipErrorInvalidValue;
+  if (L.D == 128) {
+    if (ns == 2) DA_COMBINE(128, 2);
+    else if (ns == 4) DA_COMBINE(128, 4);
+    else if (ns == 8) DA_COMBINE(128, 8);
+    else if (ns == 16) DA_COMBINE(128, 16);
+    else DA_COMBINE(128, 0);
+  } else {
+    if (ns == 2) DA_COMBINE(64, 2);
+    else if (ns == 4) DA_COMBINE(64, 4);
+    else if (ns == 8) DA_COMBINE(64, 8);
+    else if (ns == 16) DA_COMBINE(64, 16);
+    else DA_COMBINE(64, 0);
+  }
+#undef DA_COMBINE
   return hipGetLastError();
 }
 
