@@ -110,6 +110,19 @@ def test_several_query_tokens(da):
     assert "query tokens" in da.decode_attn_last_error()
 
 
+def test_slab_size_limit(da):
+    # one (batch, kv head) slab of capacity * head_dim bf16 must stay under 4 GiB:
+    # the largest capacity is 2^24 - 1 rows at head_dim 128 and 2^25 - 1 at 64
+    for D, cap in ((128, (1 << 24) - 1), (64, (1 << 25) - 1)):
+        P = plan(da, head_dim=D, capacity=cap, max_k_len=cap)
+        assert P.prob.capacity == cap
+        S = da.decode_attn_plan(2, 16, 1, D, cap, topk_max=2048, kv_batch=2, num_cus=256)
+        assert S.prob.capacity == cap
+        with pytest.raises(da.DecodeAttnError) as ei:
+            plan(da, head_dim=D, capacity=cap + 1, max_k_len=cap + 1)
+        assert ei.value.status == 2 and "4 GiB" in str(ei.value)
+
+
 def test_causal_is_accepted(da):
     a, b = plan(da, causal=True), plan(da, causal=False)
     assert (a.num_splits_max, a.chunk, a.workspace_bytes) == (b.num_splits_max, b.chunk,
