@@ -76,6 +76,14 @@ def traffic_from_counters(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def per_wave_runs(plan, B, Hkv, G, Sq) -> bool:
+    """Whether the length-balanced pass takes one run per wave: at least as many
+    key streams (sequence, kv head, head tile) as the grid has waves. A stream
+    holds the largest divisor of G whose heads times Sq fit 16 query rows."""
+    heads = max(d for d in range(1, 16 // Sq + 1) if G % d == 0)
+    return B * Hkv * (G // heads) >= plan.balanced_wgs * 4
+
+
 def build_inputs(args, torch, W, H):
     if args.workload in W.RAGGED_CASES:
         case = W.RAGGED_CASES[args.workload]
@@ -571,8 +579,10 @@ def main():
             "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
             "frac_of_measured_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
             "traffic": traffic,
-            "kernel": ("attend_balanced (length-balanced stream of K and V)" if ragged or one_call
-                       else "attend_partial (split-K stream of K and V)"),
+            "kernel": (("attend_balanced_waves (length-balanced runs of one wave each)"
+                        if per_wave_runs(plan, B, case.Hkv, Hq // case.Hkv, Sq)
+                        else "attend_balanced (length-balanced stream of K and V)")
+                       if ragged or one_call else "attend_partial (split-K stream of K and V)"),
             "kernel_us_mean": round(kern_mean_s * 1e6, 3),
             "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),

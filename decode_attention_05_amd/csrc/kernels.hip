@@ -14,7 +14,9 @@
 // head tile) key streams laid end to end. Either way the workgroup calls
 // attend_range on a key range, whose four waves each stream every fourth
 // 32-key tile and keep their own base-2 online-softmax state, merged at the
-// end; combine_splits / combine_balanced merge the partials (log-sum-exp).
+// end. attend_balanced_waves (batches with more streams than the grid has
+// waves): each wave owns a run and streams it alone (wave_stream).
+// combine_splits / combine_balanced merge the partials (log-sum-exp).
 //
 // Per 32-key tile, for the (up to 16) query rows (heads x tokens) of the tile:
 //   S^T[32 keys x 16 rows] = K_tile . Q^T  two v_mfma_f32_16x16x32_bf16 chains over D.
@@ -103,6 +105,101 @@ struct TileRegs {
   int tau;                       // tile index within the range
 };
 
+// One 32-key tile of the online softmax for the wave's 16 query rows (lane
+// group g = lane / 16, row r16 = lane % 16): V into this wave's LDS tile `vt`
+// (slots outside R.mask zeroed), the score MFMAs against the query operand qop,
+// the base-2 online softmax over the keys row r16 may see, and the P.V MFMAs
+// into O. Row r16 sees the keys of R.mask, and with `cut` only the first
+// rel - row_off of them (a causal row of several tokens). With R.mask = 0 the
+// state is left as it is (every score -inf, every V row zeroed).
+template <int D>
+__device__ __forceinline__ void tile_step(const TileRegs<D>& R, bool cut, int rel, int row_off,
+                                          const bf16x8 (&qop)[Geometry<D>::NC], unsigned char* vt,
+                                          floatx4 (&O)[Geometry<D>::NDT], float& m, float& l,
+                                          float qscale, int lane) {
+  using Gm = Geometry<D>;
+  constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
+  const int g = lane >> 4, r16 = lane & 15;
+  const uint32_t mask = R.mask;
+  // V tile -> LDS (swizzled), for the transposed reads below. Rows of masked
+  // slots are zeroed so that a non-finite value there cannot reach the output.
+  if (mask == 0xffffffffu) {
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) = R.v[r];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      const bool ok = (mask >> (idx / RU4)) & 1u;
+      *reinterpret_cast<uint4*>(vt + v_off<D>(idx / RU4, idx % RU4)) =
+          ok ? R.v[r] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // S^T halves: keys 4g+i (first) and 16+4g+i (second) for head r16.
+  floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[0][c]), qop[c], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[1][c]), qop[c], s1, 0, 0, 0);
+  }
+  uint32_t lm = mask;  // keys this lane's row may see
+  if (cut) {
+    const int n = rel - row_off;
+    lm &= n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+  }
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
+    sc[i] = ((lm >> k0) & 1u) ? s0[i] * qscale : kNegInf;
+    sc[4 + i] = ((lm >> k1) & 1u) ? s1[i] * qscale : kNegInf;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);
+  // -inf only for a row that has seen no key yet (causal rows): then every
+  // weight below is exp2(-inf) = 0 and the state stays empty.
+  const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = exp2_fast(m - m_ref);
+  uint32_t pw[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pw[i] = pack_bf16(exp2_fast(sc[2 * i] - m_ref), exp2_fast(sc[2 * i + 1] - m_ref));
+    psum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xffff0000u);
+  }
+  l = l * alpha + psum;
+  m = m_new;
+  const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  // O^T[d tile] = alpha * O^T + V^T P^T. Transposed V reads: lane (g, j = r16)
+  // addresses key 4g + (j >> 2) (+16 for the second half), d = 16 dt + 4 (j & 3);
+  // it receives V[4g + e][16 dt + j] for e = 0..3 (+16), the keys of its P slots.
+  const int jk = 4 * g + (r16 >> 2);
+  const int q4 = r16 & 3;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int chunk = 2 * dt + (q4 >> 1);
+    const int sub = (q4 & 1) * 8;
+    const shortx4 lo = lds_read_tr(vt + v_off<D>(jk, chunk) + sub);
+    const shortx4 hi = lds_read_tr(vt + v_off<D>(16 + jk, chunk) + sub);
+    const bf16x8 vop = __builtin_bit_cast(
+        bf16x8, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))));
+    O[dt] *= alpha;
+    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, O[dt], 0, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+}
+
 // Where attend_range leaves the result of its GT heads: the bf16 output rows
 // (direct: head hh at out + hh * D), or fp32 unnormalised partials with their
 // running max (base 2) and denominator (head hh at po + hh * po_stride and
@@ -126,7 +223,7 @@ struct RangeOut {
 // k_len - Sq + 1 + t. Every thread of the workgroup must call it with the same
 // arguments; it synchronises the workgroup and uses all of `lds`, so a caller
 // that calls it again first synchronises.
-template <int D, bool SPARSE, bool WAVE = false>
+template <int D, bool SPARSE>
 __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned char* lds,
                                              float (&mrg_m)[kWaves][16],
                                              float (&mrg_l)[kWaves][16], int b, int hkv,
@@ -270,6 +367,9 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   float l = 0.f;      // this lane's share of the denominator of head r16
   const float qscale = a.qscale;
 
+  // The tile update is written out here rather than shared with tile_step:
+  // through the shared function the compiler scheduled this kernel's loop
+  // differently and the long-context workload ran 1.2 % slower (same box).
   auto process_tile = [&](const TileRegs<D>& R) {
     const uint32_t mask = R.mask;
     if (mask == 0u) return;  // nothing valid: the state is left untouched
@@ -352,13 +452,12 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
-  // Wave `wave` takes tiles wave, wave + 4, ... (a wave-local range: every
-  // tile); the next tile's loads are in flight while the current one is
-  // processed.
-  constexpr int kStep = WAVE ? 1 : kWaves;
+  // Wave `wave` takes tiles wave, wave + 4, ...; the next tile's loads are in
+  // flight while the current one is processed.
+  constexpr int kStep = kWaves;
   {
     TileRegs<D> A, B;
-    int tau = WAVE ? 0 : wave;
+    int tau = wave;
     load_tile(A, tau);
     while (tau < ntiles) {
       load_tile(B, tau + kStep);
@@ -374,33 +473,6 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   // Denominator of head r16 over the four lane groups.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-
-  if constexpr (WAVE) {
-    // One wave owns the range: lane (g, r16) holds values 16 dt + 4 g .. + 3
-    // of row r16 and writes them itself, with no merge and no barrier.
-    if (r16 < RT) {
-      if (ro.direct) {
-        const float inv = (l > 0.f) ? 1.f / l : 0.f;
-        uint16_t* dst = ro.out + (int64_t)r16 * D + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          *reinterpret_cast<uint2*>(dst + 16 * dt) =
-              make_uint2(pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
-                         pack_bf16(O[dt][2] * inv, O[dt][3] * inv));
-      } else {
-        float* po = ro.po + r16 * ro.po_stride + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          *reinterpret_cast<float4*>(po + 16 * dt) =
-              make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
-        if (g == 0) {
-          ro.pm[r16 * ro.pm_stride] = m;
-          ro.pl[r16 * ro.pm_stride] = l;
-        }
-      }
-    }
-    return;
-  }
 
   __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
   float* mo = reinterpret_cast<float*>(lds);
@@ -520,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_partial(PartialLaunch a) {
 // 32-key tiles, laid end to end sequence by sequence (shortest first for up to
 // 64 sequences, see length_order; index order beyond), then kv head, then head
 // tile.
-// Run w (a workgroup, or a wave when streams are many, see wave_runs) takes
+// Run w (a workgroup, or a wave when streams are many, see runs_per_wave) takes
 // tiles [w * per_run, (w + 1) * per_run) of that concatenation, so every run
 // streams the same number of tiles whatever the mix of lengths. A stream that
 // lies inside one run is finished there (bf16 output); a stream cut by a run
@@ -559,16 +631,15 @@ __device__ __forceinline__ int64_t run_tiles(int64_t total, int64_t runs) {
   return even > kMinTilesPerRun ? even : kMinTilesPerRun;
 }
 
-// Runs: one per workgroup, or one per wave when there are at least as many
-// non-empty streams as waves. With many short streams a workgroup's run cuts
-// through several of them, and every piece costs the four waves a pipeline
-// fill and a merge behind a barrier; one wave per run streams its pieces alone,
-// writes its own rows, and its bubbles are filled by the CU's other waves
-// (measured on 512 sequences of 128 to 2048 keys, 8 kv heads: 4,775 GB/s with a
-// run per workgroup, 5,651 GB/s with a run per wave, merge included).
-__device__ __forceinline__ bool wave_runs(const PartialLaunch& a, int64_t nonempty_seqs,
-                                          int streams_per_seq) {
-  return nonempty_seqs * streams_per_seq >= (int64_t)a.balanced_wgs * kWaves;
+// Runs: one per workgroup, or one per wave when the batch has at least as many
+// key streams as the grid has waves. With many short streams a workgroup's run
+// cuts through several of them, and every piece costs the four waves a merge
+// behind a barrier; one wave per run streams its pieces alone (wave_stream),
+// with the next piece's loads in flight while it finishes one, and writes its
+// own rows. Decided from the shapes alone, the same way on the host (which
+// kernel to launch) and in the merge.
+__host__ __device__ __forceinline__ bool runs_per_wave(const PartialLaunch& a) {
+  return (int64_t)a.B * a.Hkv * (a.G / a.heads_per_wg) >= (int64_t)a.balanced_wgs * kWaves;
 }
 
 // More than 64 sequences are read kLenGroup at a time, kLenGroup / 64 per
@@ -587,21 +658,17 @@ __device__ __forceinline__ void load_lengths(const PartialLaunch& a, int base,
   }
 }
 
-// Tiles over all streams and the number of non-empty sequences, sequences in
-// index order (more than 64 sequences).
-__device__ __forceinline__ int64_t total_tiles(const PartialLaunch& a, int streams_per_seq,
-                                               int64_t* nonempty) {
-  int64_t mine = 0, live = 0;
+// Tiles over all streams (more than 64 sequences).
+__device__ __forceinline__ int64_t total_tiles(const PartialLaunch& a, int streams_per_seq) {
+  int64_t mine = 0;
   for (int base = 0; base < a.B; base += kLenGroup) {
     int len[kLenSlots];
     load_lengths(a, base, len);
 #pragma unroll
     for (int i = 0; i < kLenSlots; ++i) {
       mine += tiles_of(len[i]);
-      live += len[i] > 0 ? 1 : 0;
     }
   }
-  *nonempty = uniform_i64(wave_sum_i64(live));
   return uniform_i64(wave_sum_i64(mine)) * streams_per_seq;
 }
 
@@ -643,69 +710,83 @@ __device__ __forceinline__ SeqOrder length_order(const PartialLaunch& a, int str
   return o;
 }
 
-// The pieces of run `run` (tiles [run * per_run, (run + 1) * per_run) of the
-// concatenation): the whole workgroup (WAVE false) or one wave (WAVE true)
-// walks them.
-template <int D, bool WAVE>
+// The sequence whose streams hold tile t0 (< total) of the concatenation, and
+// the first tile of its streams. Returns false only if no sequence does, which
+// the schedule rules out.
+__device__ __forceinline__ bool locate(const PartialLaunch& a, int64_t t0, int per_seq,
+                                       bool by_length, const SeqOrder& o, int& b,
+                                       int64_t& seq_start) {
+  const int lane = threadIdx.x & 63;
+  b = 0;
+  seq_start = 0;
+  if (by_length) {
+    const int64_t n = tiles_of(o.len) * per_seq;
+    const uint64_t hit = __ballot(lane < a.B && n > 0 && o.before <= t0 && t0 < o.before + n);
+    if (hit == 0) return false;
+    b = __builtin_ctzll(hit);
+    seq_start = uniform_i64(__shfl(o.before, b));
+    return true;
+  }
+  // Index order: the first b with per_seq * (tiles before b) <= t0 <
+  // per_seq * (tiles up to b), 64 sequences per step, lane-parallel scan.
+  int64_t acc = 0;
+  bool found = false;
+  for (int base = 0; base < a.B && !found; base += kLenGroup) {
+    int len[kLenSlots];
+    load_lengths(a, base, len);
+#pragma unroll
+    for (int i = 0; i < kLenSlots; ++i) {
+      if (found) break;
+      const int64_t n = tiles_of(len[i]) * per_seq;
+      int64_t inc = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      inc += acc;
+      const int64_t exc = inc - n;
+      const uint64_t hit = __ballot(n > 0 && exc <= t0 && t0 < inc);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        b = base + 64 * i + src;
+        seq_start = uniform_i64(__shfl(exc, src));
+        found = true;
+      }
+      acc = uniform_i64(__shfl(inc, 63));
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  return found;
+}
+
+// Live length of sequence bb as a wave-uniform value: from the lanes of the
+// length order (up to 64 sequences) or from memory.
+__device__ __forceinline__ int64_t uniform_len(const PartialLaunch& a, bool by_length,
+                                               const SeqOrder& o, int bb) {
+  return by_length ? (int64_t)__builtin_amdgcn_readlane(o.len, bb)
+                   : (int64_t)__builtin_amdgcn_readfirstlane(seq_len(a, bb));
+}
+
+// The pieces of workgroup run `run` (tiles [run * per_run, (run + 1) * per_run)
+// of the concatenation), one attend_range call per piece.
+template <int D>
 __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char* lds,
                                            float (&mrg_m)[kWaves][16],
                                            float (&mrg_l)[kWaves][16], int64_t run,
                                            int64_t per_run, int64_t total, int per_seq,
                                            bool by_length, const SeqOrder& o) {
-  const int lane = threadIdx.x & 63;
   const int GT = a.heads_per_wg;
   const int RT = GT * a.Sq;             // query rows of one stream
   const int tiles_h = a.G / GT;
   const int64_t t0 = run * per_run;
-  if (t0 >= total) return;  // the whole workgroup (or wave) leaves together
+  if (t0 >= total) return;  // the whole workgroup leaves together
   const int64_t t1 = (t0 + per_run < total) ? t0 + per_run : total;
 
-  // The sequence whose streams hold tile t0.
-  int b = 0;
-  int64_t seq_start = 0;  // first tile of sequence b's streams
-  if (by_length) {
-    const int64_t n = tiles_of(o.len) * per_seq;
-    const uint64_t hit = __ballot(lane < a.B && n > 0 && o.before <= t0 && t0 < o.before + n);
-    if (hit == 0) return;  // unreachable: t0 < total lies in a non-empty sequence
-    b = __builtin_ctzll(hit);
-    seq_start = uniform_i64(__shfl(o.before, b));
-  } else {
-    // Index order: the first b with per_seq * (tiles before b) <= t0 <
-    // per_seq * (tiles up to b), 64 sequences per step, lane-parallel scan.
-    int64_t acc = 0;
-    bool found = false;
-    for (int base = 0; base < a.B && !found; base += kLenGroup) {
-      int len[kLenSlots];
-      load_lengths(a, base, len);
-#pragma unroll
-      for (int i = 0; i < kLenSlots; ++i) {
-        if (found) break;
-        const int64_t n = tiles_of(len[i]) * per_seq;
-        int64_t inc = n;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int64_t y = __shfl_up(inc, off);
-          if (lane >= off) inc += y;
-        }
-        inc += acc;
-        const int64_t exc = inc - n;
-        const uint64_t hit = __ballot(n > 0 && exc <= t0 && t0 < inc);
-        if (hit) {
-          const int src = __builtin_ctzll(hit);
-          b = base + 64 * i + src;
-          seq_start = uniform_i64(__shfl(exc, src));
-          found = true;
-        }
-        acc = uniform_i64(__shfl(inc, 63));
-      }
-    }
-  }
-  b = __builtin_amdgcn_readfirstlane(b);
-  auto length_of = [&](int bb) -> int64_t {
-    return by_length ? (int64_t)__builtin_amdgcn_readlane(o.len, bb)
-                     : (int64_t)__builtin_amdgcn_readfirstlane(seq_len(a, bb));
-  };
-  int64_t len = length_of(b);
+  int b;
+  int64_t seq_start;  // first tile of sequence b's streams
+  if (!locate(a, t0, per_seq, by_length, o, b, seq_start)) return;
+  int64_t len = uniform_len(a, by_length, o, b);
   int64_t nb = tiles_of(len);  // tiles of each stream of sequence b
   if (nb == 0) return;         // unreachable: t0 < total lies in a non-empty sequence
   const int64_t rel = t0 - seq_start;
@@ -727,12 +808,12 @@ __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char
     ro.po_stride = D;
     ro.pm_stride = 1;
     const int64_t j1 = (jt + nt) * kTileKeys;
-    attend_range<D, false, WAVE>(a, lds, mrg_m, mrg_l, b, hkv, row0, RT, len, jt * kTileKeys,
-                                 j1 < len ? j1 : len, ro);
+    attend_range<D, false>(a, lds, mrg_m, mrg_l, b, hkv, row0, RT, len, jt * kTileKeys,
+                           j1 < len ? j1 : len, ro);
     x += nt;
     if (x >= t1) break;
     // the merge area is read before the next range's V tiles land there
-    if constexpr (!WAVE) __syncthreads();
+    __syncthreads();
     // Next stream: the next head tile / kv head, else the next non-empty sequence.
     jt = 0;
     if (++r == per_seq) {
@@ -740,7 +821,7 @@ __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char
       do {
         b = by_length ? __builtin_amdgcn_readlane(o.next, b) : b + 1;
         if (b >= a.B) break;
-        len = length_of(b);
+        len = uniform_len(a, by_length, o, b);
         nb = tiles_of(len);
       } while (nb == 0);
       if (b >= a.B) break;  // unreachable: tiles remain before t1 <= total
@@ -748,38 +829,363 @@ __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char
   }
 }
 
-// MAY_WAVE: the batch has enough streams for one run per wave to be possible
-// (decided on the host from the shapes; the lengths decide on the device). A
-// batch that cannot qualify gets a kernel without the per-wave path, whose
-// registers the workgroup path then has to itself.
-template <int D, bool MAY_WAVE>
+// LDS bytes per wave that hold finished pieces of a run until the run ends. A
+// record is a 16-byte header (first query row, flags, record bytes) and then
+// either the bf16 output rows [RT][D] of a whole stream or the fp32 partial
+// rows [RT][D] followed by (m, l) per row; the largest (16 partial rows at
+// D = 128) fits. Four waves' buffers and V tiles take 80 KiB at D = 128, so
+// two workgroups share a CU's 160 KiB.
+constexpr int kPieceBufBytes = 12288;
+
+// Per-tile facts of the wave streamer (uniform across the wave).
+constexpr int kTileFirst = 1;    // first tile of its piece: the softmax state starts empty
+constexpr int kTileLast = 2;     // last tile of its piece: the piece's rows are written
+constexpr int kTileDirect = 4;   // the piece is its whole stream: bf16 output
+constexpr int kTileSlot1 = 8;    // the piece starts after the run does: partial slot 1
+constexpr int kTileReal = 16;    // a tile of the run (else a re-read past its end)
+
+template <int D>
+struct StreamTile {
+  TileRegs<D> t;                 // K, V and the key mask
+  bf16x8 q[Geometry<D>::NC];     // the piece's query rows (B operand of the scores)
+  int row0;                      // first query row of the tile's stream (q / out rows)
+  int lim;                       // keys from the tile's first to its sequence's length,
+                                 // at most 64 (several causal tokens; 64: no mask)
+  int flags;
+};
+
+// Run `run` of one wave (tiles [t0, t1) of the concatenation) streamed as one
+// tile sequence: the loads of the next tile are in flight while the current one
+// is processed, across stream boundaries too. Every tile carries its own copy
+// of its stream's query rows (loaded with its K and V, cached), so every load
+// is unconditional and no register that a queued tile still needs is
+// overwritten. A piece (the part of a stream inside the run) starts from an
+// empty softmax state at its first tile and ends with a record of its rows:
+// bf16 output for a whole stream, else an fp32 partial for slot 0 (the piece
+// that starts the run) or 1 (the one that ends it) of the run.
+// The records wait in the wave's LDS buffer `pb` and are written out when it
+// is full and when the run ends. A global store issued between tile loads sits
+// in the same in-order memory counter as the loads, so the wait for every tile
+// loaded after it also waits for the store's acknowledgement, which under a
+// full read stream takes about one loaded memory latency.
+template <int D>
+__device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned char* vt,
+                                            unsigned char* pb, int64_t run, int64_t per_run,
+                                            int64_t total, int per_seq, bool by_length,
+                                            const SeqOrder& o) {
+  using Gm = Geometry<D>;
+  constexpr int NC = Gm::NC, NDT = Gm::NDT, VLD = Gm::VLD, RU4 = Gm::RU4;
+  const int64_t t0 = run * per_run;
+  if (t0 >= total) return;  // the wave leaves
+  const int64_t t1 = (t0 + per_run < total) ? t0 + per_run : total;
+
+  // The per-lane values of the process step are derived afresh in every step
+  // from an opaque copy of the lane id, so that they are not kept live (and
+  // spilled) across the whole tile loop; the load addresses are derived once.
+  auto fresh_lane = []() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t & 63;
+  };
+  const int GT = a.heads_per_wg, RT = GT * a.Sq, tiles_h = a.G / GT;
+  const bool causal_rows = a.causal && a.Sq > 1;
+  const float qscale = a.qscale;
+  // Per-lane byte offset inside the query rows of a stream, fixed for the run.
+  // Query lanes past the stream's RT rows read its last row: their columns of
+  // the score and output tiles are never written out.
+  const int lane_ld = threadIdx.x & 63;
+  const uint32_t q_lane =
+      (uint32_t)((lane_ld & 15) < RT ? (lane_ld & 15) : RT - 1) * Gm::ROWB + (uint32_t)(lane_ld >> 4) * 16u;
+
+  // The load cursor: tile x of the concatenation, tile jt of stream r of
+  // sequence cb (length clen, cnb tiles per stream). Past the run it stays on
+  // the run's last tile, which the extra load at the end re-reads.
+  int cb;
+  int64_t seq_start;
+  if (!locate(a, t0, per_seq, by_length, o, cb, seq_start)) return;
+  // More than 64 sequences: the lengths of sequences len_base .. len_base + 63,
+  // one per lane (0 past the batch), so that moving to the next sequence reads
+  // a lane instead of waiting on a load (which would drain every tile load in
+  // flight); reloaded once per 64 sequences.
+  int len_base = cb & ~63;
+  int len_win = 0;
+  auto load_len_win = [&]() {
+    const int bb = len_base + lane_ld;
+    len_win = bb < a.B ? (int)seq_len(a, bb) : 0;
+  };
+  if (!by_length) load_len_win();
+  auto next_len = [&](int bb) -> int64_t {
+    if (by_length) return (int64_t)__builtin_amdgcn_readlane(o.len, bb);
+    if (bb >= len_base + 64) {
+      len_base = bb & ~63;
+      load_len_win();
+    }
+    return (int64_t)__builtin_amdgcn_readlane(len_win, bb - len_base);
+  };
+  int64_t clen = next_len(cb);
+  int64_t cnb = tiles_of(clen);
+  if (cnb == 0) return;  // unreachable: t0 < total lies in a non-empty sequence
+  int cr = (int)((t0 - seq_start) / cnb);
+  int64_t cjt = (t0 - seq_start) - (int64_t)cr * cnb;
+  int64_t cx = t0;
+
+  auto advance = [&]() {
+    if (cx + 1 >= t1) {
+      cx = t1;
+      return;
+    }
+    ++cx;
+    if (++cjt < cnb) return;
+    if (cr + 1 < per_seq) {
+      ++cr;
+      cjt = 0;
+      return;
+    }
+    int nbq = cb;
+    int64_t nlen = 0, nnb = 0;
+    for (;;) {
+      nbq = by_length ? __builtin_amdgcn_readlane(o.next, nbq) : nbq + 1;
+      if (nbq >= a.B) {  // unreachable: tiles remain before t1 <= total
+        cx = t1;
+        cjt = cnb - 1;
+        return;
+      }
+      nlen = next_len(nbq);
+      nnb = tiles_of(nlen);
+      if (nnb > 0) break;
+    }
+    cb = nbq;
+    clen = nlen;
+    cnb = nnb;
+    cr = 0;
+    cjt = 0;
+  };
+
+  // Paged cache: block-table entries pg_first .. pg_first + 63 of sequence
+  // pg_b, one per lane.
+  int pg_b = -1, pg_first = 0, pg_ids = -1;
+
+  auto load = [&](StreamTile<D>& T) {
+    const int lane = lane_ld;
+    const int g = lane >> 4, r16 = lane & 15;
+    const bool real = cx < t1;
+    const int hkv = cr / tiles_h, ht = cr - hkv * tiles_h;
+    const int64_t kt = cjt * kTileKeys;
+    const int64_t left = clen - kt;  // >= 1: the cursor is on a tile of the stream
+    const int nv = left >= kTileKeys ? kTileKeys : (int)left;
+    const int last = nv - 1;
+    T.t.mask = real ? (nv == kTileKeys ? 0xffffffffu : ((1u << nv) - 1u)) : 0u;
+    T.row0 = (int)(((int64_t)cb * a.Hq + hkv * a.G + ht * GT) * a.Sq);
+    T.lim = causal_rows ? (left >= 64 ? 64 : (int)left) : 64;
+    const int64_t sfirst = cx - cjt;  // the stream's first tile in the concatenation
+    T.flags = (real ? kTileReal : 0) | ((cjt == 0 || cx == t0) ? kTileFirst : 0) |
+              ((cjt == cnb - 1 || cx == t1 - 1) ? kTileLast : 0) |
+              ((sfirst >= t0 && sfirst + cnb <= t1) ? kTileDirect : 0) |
+              (sfirst > t0 ? kTileSlot1 : 0);
+    {
+      const unsigned char* qb = reinterpret_cast<const unsigned char*>(a.q + (int64_t)T.row0 * D);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        T.q[c] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + q_lane + 64u * c));
+    }
+    const unsigned char* kb;
+    const unsigned char* vb;
+    if (a.block_table) {
+      // A 32-key tile lies inside one page; a page id outside [0, num_pages) is
+      // never read (the tile is dropped and its loads go to page 0).
+      const int lp = (int)((uint32_t)kt / (uint32_t)a.page_size);  // kt < 2^31
+      int64_t page;
+      if (cb != pg_b || lp < pg_first || lp >= pg_first + 64) {
+        pg_b = cb;
+        pg_first = lp;
+        const int e = lp + lane;
+        pg_ids = e < a.max_pages ? a.block_table[(int64_t)cb * a.max_pages + e] : -1;
+        page = __builtin_amdgcn_readlane(pg_ids, 0);
+      } else {
+        page = __builtin_amdgcn_readlane(pg_ids, lp - pg_first);
+      }
+      if (page < 0 || page >= a.num_pages) {
+        page = 0;
+        T.t.mask = 0u;
+      }
+      const int64_t in_page = kt - (int64_t)lp * a.page_size;
+      const int64_t off = ((page * a.Hkv + hkv) * a.page_size + in_page) * Gm::ROWB;
+      kb = reinterpret_cast<const unsigned char*>(a.k) + off;
+      vb = reinterpret_cast<const unsigned char*>(a.v) + off;
+    } else {
+      const int64_t off = (((int64_t)cb * a.Hkv + hkv) * a.capacity + kt) * Gm::ROWB;
+      kb = reinterpret_cast<const unsigned char*>(a.k) + off;
+      vb = reinterpret_cast<const unsigned char*>(a.v) + off;
+    }
+    // Slots past the stream's last key (its last tile) re-read that key.
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int slot = 16 * sb + r16;
+      const uint32_t row = (uint32_t)(slot < last ? slot : last);
+      const uint32_t off = row * (uint32_t)Gm::ROWB + (uint32_t)g * 16u;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) T.t.k[sb][c] = load_stream(kb, off + 64u * c);
+    }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      const int slot = idx / RU4, chunk = idx % RU4;
+      const uint32_t row = (uint32_t)(slot < last ? slot : last);
+      T.t.v[r] = load_stream(vb, row * (uint32_t)Gm::ROWB + (uint32_t)chunk * 16u);
+    }
+  };
+
+  // Records of finished pieces held in pb (pb_used bytes), written out by
+  // flush: bf16 rows for a whole stream, else the fp32 partial with its (m, l)
+  // in the run's slot.
+  const int direct_bytes = 16 + RT * D * 2;
+  const int partial_bytes = (16 + RT * D * 4 + RT * 8 + 15) & ~15;  // headers 16-byte aligned
+  int pb_used = 0;
+  auto flush = [&]() {
+    const int lane = fresh_lane();
+    const int g = lane >> 4, r16 = lane & 15;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    for (int at = 0; at < pb_used;) {
+      const unsigned char* rec = pb + at;
+      const int4 h = *reinterpret_cast<const int4*>(rec);
+      const int row0 = __builtin_amdgcn_readfirstlane(h.x);
+      const int fl = __builtin_amdgcn_readfirstlane(h.y);
+      at += __builtin_amdgcn_readfirstlane(h.z);
+      if (r16 < RT) {
+        if (fl & kTileDirect) {
+          const uint2* src = reinterpret_cast<const uint2*>(rec + 16) + (r16 * D + 4 * g) / 4;
+          uint16_t* dst = a.out + ((int64_t)row0 + r16) * D + 4 * g;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<uint2*>(dst + 16 * dt) = src[4 * dt];
+        } else {
+          const float4* src = reinterpret_cast<const float4*>(rec + 16) + (r16 * D + 4 * g) / 4;
+          const float2 ml = *reinterpret_cast<const float2*>(rec + 16 + RT * D * 4 + r16 * 8);
+          const int64_t slot = (run * 2 + ((fl & kTileSlot1) ? 1 : 0)) * RT + r16;
+          float* po = a.part_o + slot * D + 4 * g;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<float4*>(po + 16 * dt) = src[4 * dt];
+          if (g == 0) {
+            a.part_m[slot] = ml.x;
+            a.part_l[slot] = ml.y;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    pb_used = 0;
+  };
+
+  floatx4 O[NDT];
+  float m = kNegInf, l = 0.f;
+  auto process = [&](const StreamTile<D>& T) {
+    const int lane = fresh_lane();
+    const int g = lane >> 4, r16 = lane & 15;
+    if (T.flags & kTileFirst) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m = kNegInf;
+      l = 0.f;
+    }
+    // Every processed tile goes through the update, also one without a valid
+    // key (a page id out of range), which leaves the state as it is (its V
+    // rows are zeroed and every score is -inf): one path, on which every load
+    // of the tile is consumed.
+    // row r16 sees T.lim - row_off keys of this tile (later tokens see more)
+    tile_step<D>(T.t, T.lim < 64, T.lim, a.Sq - 1 - r16 % a.Sq, T.q, vt, O, m, l, qscale, lane);
+    if (T.flags & kTileLast) {
+      // The piece's record: lane (g, r16) holds values 16 dt + 4 g .. + 3 of row r16.
+      float lt = l + __shfl_xor(l, 16);
+      lt += __shfl_xor(lt, 32);
+      const bool direct = (T.flags & kTileDirect) != 0;
+      const int bytes = direct ? direct_bytes : partial_bytes;
+      if (pb_used + bytes > kPieceBufBytes) flush();
+      unsigned char* rec = pb + pb_used;
+      if (lane == 0) *reinterpret_cast<int4*>(rec) = make_int4(T.row0, T.flags, bytes, 0);
+      if (r16 < RT) {
+        if (direct) {
+          const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+          uint2* dst = reinterpret_cast<uint2*>(rec + 16) + (r16 * D + 4 * g) / 4;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            dst[4 * dt] = make_uint2(pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
+                                     pack_bf16(O[dt][2] * inv, O[dt][3] * inv));
+        } else {
+          float4* dst = reinterpret_cast<float4*>(rec + 16) + (r16 * D + 4 * g) / 4;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            dst[4 * dt] = make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
+          if (g == 0)
+            *reinterpret_cast<float2*>(rec + 16 + RT * D * 4 + r16 * 8) = make_float2(m, lt);
+        }
+      }
+      pb_used += bytes;
+    }
+  };
+
+  // Two tiles in flight: each one's registers are refilled right after it is
+  // processed (a tile past the run is loaded but never processed).
+  StreamTile<D> A, B;
+  load(A);
+  advance();
+  load(B);
+  advance();
+  for (;;) {
+    process(A);
+    if (!(B.flags & kTileReal)) break;
+    load(A);
+    advance();
+    process(B);
+    if (!(A.flags & kTileReal)) break;
+    load(B);
+    advance();
+  }
+  flush();
+}
+
+// Length-balanced pass, one run per workgroup.
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attend_balanced(PartialLaunch a) {
   using Gm = Geometry<D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS];
   __shared__ float mrg_m[kWaves][16];
   __shared__ float mrg_l[kWaves][16];
 
-  const int lane = threadIdx.x & 63;
   const int per_seq = a.Hkv * (a.G / a.heads_per_wg);  // streams per sequence
   const bool by_length = a.B <= 64;
   SeqOrder o{};
-  int64_t total, nonempty;
+  int64_t total;
   if (by_length) {
     o = length_order(a, per_seq);
     total = o.total;
-    nonempty = __builtin_popcountll(__ballot(lane < a.B && o.len > 0));
   } else {
-    total = total_tiles(a, per_seq, &nonempty);
+    total = total_tiles(a, per_seq);
   }
-  if (MAY_WAVE && wave_runs(a, nonempty, per_seq)) {
-    const int64_t runs = (int64_t)a.balanced_wgs * kWaves;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    run_pieces<D, true>(a, lds, mrg_m, mrg_l, (int64_t)blockIdx.x * kWaves + wave,
-                        run_tiles(total, runs), total, per_seq, by_length, o);
+  run_pieces<D>(a, lds, mrg_m, mrg_l, (int64_t)blockIdx.x, run_tiles(total, a.balanced_wgs),
+                total, per_seq, by_length, o);
+}
+
+// Length-balanced pass, one run per wave (runs_per_wave).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attend_balanced_waves(PartialLaunch a) {
+  using Gm = Geometry<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * (Gm::VTILE + kPieceBufBytes)];
+
+  const int per_seq = a.Hkv * (a.G / a.heads_per_wg);  // streams per sequence
+  const bool by_length = a.B <= 64;
+  SeqOrder o{};
+  int64_t total;
+  if (by_length) {
+    o = length_order(a, per_seq);
+    total = o.total;
   } else {
-    run_pieces<D, false>(a, lds, mrg_m, mrg_l, (int64_t)blockIdx.x,
-                         run_tiles(total, a.balanced_wgs), total, per_seq, by_length, o);
+    total = total_tiles(a, per_seq);
   }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t runs = (int64_t)a.balanced_wgs * kWaves;
+  wave_stream<D>(a, lds + wave * Gm::VTILE, lds + kWaves * Gm::VTILE + wave * kPieceBufBytes,
+                 (int64_t)blockIdx.x * kWaves + wave, run_tiles(total, runs), total, per_seq,
+                 by_length, o);
 }
 
 // Merge of the partials of one stream (b, kv head, head tile) cut by the
@@ -804,7 +1210,7 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
 
   // The schedule of attend_balanced: every tile, and the tiles laid before
   // sequence b's streams (shortest first up to 64 sequences, else index order).
-  int64_t total, before_b, nonempty;
+  int64_t total, before_b;
   if (a.B <= 64) {
     // the sequences laid before b: shorter ones, and equal ones of lower index
     const int len = lane < a.B ? (int)seq_len(a, lane) : 0;
@@ -812,9 +1218,8 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
     const bool earlier = lane < a.B && (len < len_b || (len == len_b && lane < b));
     total = uniform_i64(wave_sum_i64(lane < a.B ? tiles_of(len) : 0)) * per_seq;
     before_b = uniform_i64(wave_sum_i64(earlier ? tiles_of(len) : 0)) * per_seq;
-    nonempty = __builtin_popcountll(__ballot(lane < a.B && len > 0));
   } else {
-    int64_t all = 0, before = 0, live = 0;
+    int64_t all = 0, before = 0;
     for (int base = 0; base < a.B; base += kLenGroup) {
       int len[kLenSlots];
       load_lengths(a, base, len);
@@ -823,14 +1228,12 @@ __global__ __launch_bounds__(256) void combine_balanced(PartialLaunch a) {
         const int64_t n = tiles_of(len[i]);
         all += n;
         before += base + 64 * i + lane < b ? n : 0;
-        live += n > 0 ? 1 : 0;
       }
     }
     total = uniform_i64(wave_sum_i64(all)) * per_seq;
     before_b = uniform_i64(wave_sum_i64(before)) * per_seq;
-    nonempty = uniform_i64(wave_sum_i64(live));
   }
-  const int64_t runs = wave_runs(a, nonempty, per_seq) ? (int64_t)a.balanced_wgs * kWaves
+  const int64_t runs = runs_per_wave(a) ? (int64_t)a.balanced_wgs * kWaves
                                                       : (int64_t)a.balanced_wgs;
   const int64_t per_run = run_tiles(total, runs);
   const int64_t nb = tiles_of(seq_len(a, b));
@@ -978,13 +1381,12 @@ hipError_t launch_partial_d(const PartialLaunch& L, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_balanced_d(const PartialLaunch& L, hipStream_t stream) {
-  const int64_t streams = (int64_t)L.B * L.Hkv * (L.G / L.heads_per_wg);
-  if (streams >= (int64_t)L.balanced_wgs * kWaves)
-    hipLaunchKernelGGL((attend_balanced<D, true>), dim3((unsigned)L.balanced_wgs), dim3(kThreads),
+  if (runs_per_wave(L))
+    hipLaunchKernelGGL(attend_balanced_waves<D>, dim3((unsigned)L.balanced_wgs), dim3(kThreads),
                        0, stream, L);
   else
-    hipLaunchKernelGGL((attend_balanced<D, false>), dim3((unsigned)L.balanced_wgs),
-                       dim3(kThreads), 0, stream, L);
+    hipLaunchKernelGGL(attend_balanced<D>, dim3((unsigned)L.balanced_wgs), dim3(kThreads), 0,
+                       stream, L);
   return hipGetLastError();
 }
 

@@ -341,8 +341,8 @@ def test_length_order_boundaries(da, B, num_cus, Sq, ties):
     (30, 64, 1, 128, 2, 2, True),     # 64 heads on one kv head: 8 head tiles, paged
 ])
 def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
-    # at least as many non-empty streams as waves: every wave walks its own run
-    # and writes its own rows or partials, with no workgroup merge
+    # at least as many streams as the grid has waves: every wave streams its own
+    # run and writes its own rows or partials, with no workgroup merge
     import torch
     cap, page = 640, 64
     rng = np.random.Generator(np.random.PCG64(470 + B))
@@ -385,8 +385,9 @@ def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
 
 
 def test_few_live_streams_in_a_wide_batch(da):
-    # 512 sequences x 8 kv heads could give one run per wave, but only 90 are
-    # non-empty (720 streams): the per-workgroup runs of the same kernel
+    # 512 sequences x 8 kv heads take one run per wave, but only 90 sequences
+    # are non-empty (720 streams): runs skip runs of empty sequences, across the
+    # 64-sequence windows of lengths each wave keeps, and most runs are empty
     import torch
     B, Hq, Hkv, D, cap = 512, 16, 8, 64, 300
     rng = np.random.Generator(np.random.PCG64(480))
