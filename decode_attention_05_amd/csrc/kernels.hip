@@ -973,7 +973,9 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
     const int64_t kt = cjt * kTileKeys;
     const int64_t left = clen - kt;  // >= 1: the cursor is on a tile of the stream
     const int nv = left >= kTileKeys ? kTileKeys : (int)left;
-    const int last = nv - 1;
+    // The re-read past the run reads only the last tile's last key row.
+    const int last = real ? nv - 1 : 0;
+    const int64_t row0_ld = real ? kt : kt + nv - 1;
     T.t.mask = real ? (nv == kTileKeys ? 0xffffffffu : ((1u << nv) - 1u)) : 0u;
     T.row0 = (int)(((int64_t)cb * a.Hq + hkv * a.G + ht * GT) * a.Sq);
     T.lim = causal_rows ? (left >= 64 ? 64 : (int)left) : 64;
@@ -1008,12 +1010,12 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
         page = 0;
         T.t.mask = 0u;
       }
-      const int64_t in_page = kt - (int64_t)lp * a.page_size;
+      const int64_t in_page = row0_ld - (int64_t)lp * a.page_size;  // same page as kt
       const int64_t off = ((page * a.Hkv + hkv) * a.page_size + in_page) * Gm::ROWB;
       kb = reinterpret_cast<const unsigned char*>(a.k) + off;
       vb = reinterpret_cast<const unsigned char*>(a.v) + off;
     } else {
-      const int64_t off = (((int64_t)cb * a.Hkv + hkv) * a.capacity + kt) * Gm::ROWB;
+      const int64_t off = (((int64_t)cb * a.Hkv + hkv) * a.capacity + row0_ld) * Gm::ROWB;
       kb = reinterpret_cast<const unsigned char*>(a.k) + off;
       vb = reinterpret_cast<const unsigned char*>(a.v) + off;
     }
