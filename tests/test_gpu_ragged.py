@@ -384,6 +384,30 @@ def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
     assert not got[~ref.any(axis=-1)].any()
 
 
+def test_wave_runs_of_many_short_streams(da):
+    # 1024 sequences of 1 to 70 keys, 8 kv heads, D = 128: ~8 tiles per run cut
+    # into up to eight whole streams, more finished pieces than a wave's record
+    # buffer holds (written out mid-run), and runs that move across several
+    # 64-sequence windows of lengths
+    import torch
+    B, Hq, Hkv, D, cap = 1024, 32, 8, 128, 96
+    rng = np.random.Generator(np.random.PCG64(490))
+    lens = [int(x) for x in rng.integers(1, 71, size=B)]
+    lens[::37] = [0] * len(lens[::37])
+    sq, sk, sv, _ = W.seeds(491)
+    q = W.normal_bf16(sq, (B, Hq, 1, D))
+    k = W.normal_bf16(sk, (B, Hkv, cap, D))
+    v = W.normal_bf16(sv, (B, Hkv, cap, D))
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
+    assert B * Hkv >= plan.balanced_wgs * 4   # one run per wave
+    out = _out(B, Hq, D)
+    H.log(f"wave runs of many short streams B={B} wgs={plan.balanced_wgs}")
+    da.decode_attn_dense_ragged(plan, H.to_dev(q), H.to_dev(k), H.to_dev(v), out, 0.1,
+                                H.to_dev_i32(lens), workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    _check_ragged(H.from_dev(out), q, k, v, 0.1, lens, "many short streams")
+
+
 def test_few_live_streams_in_a_wide_batch(da):
     # 512 sequences x 8 kv heads take one run per wave, but only 90 sequences
     # are non-empty (720 streams): runs skip runs of empty sequences, across the
