@@ -1,8 +1,9 @@
 """GPU parity at the largest addresses the library accepts.
 
 Every KV buffer here is larger than 4 GiB, so the (batch, kv head) slabs,
-pages and selected rows that the kernels read lie beyond what a 32-bit byte
-offset from the buffer's start can reach; the sparse case also reads the last
+pages and selected rows that the kernels (split-K, length-balanced per
+workgroup and per wave, sparse) read lie beyond what a 32-bit byte offset from
+the buffer's start can reach; the sparse case also reads the last
 rows of the largest slab a plan allows (capacity * head_dim * 2 bytes just under
 4 GiB, the limit the plan call enforces). Rows that are never written hold NaN,
 so a read of any of them would show in the output.
@@ -96,6 +97,34 @@ def test_ragged_caches_beyond_4gib(da, big_cache):
     torch.cuda.synchronize()
     H.check_tolerance(H.from_dev(out), oracle.dense_ragged(q, k, v, SCALE, lens, causal=True),
                       "ragged beyond 4 GiB")
+
+
+def test_wave_runs_over_caches_beyond_4gib(da):
+    # 640 sequences x 8 kv heads of 4096-row slabs (1 MiB each, 5 GiB per cache):
+    # one run per wave, and the slabs of sequences 512 and up start past 4 GiB.
+    import torch
+    B, Hq, Hkv, cap, live = 640, 32, 8, 4096, 160
+    rng = np.random.Generator(np.random.PCG64(35))
+    lens = rng.integers(1, live + 1, size=B).astype(np.int32)
+    sq, sk, sv, _ = W.seeds(36)
+    q = W.normal_bf16(sq, (B, Hq, 1, D))
+    k = W.normal_bf16(sk, (B, Hkv, live, D))
+    v = W.normal_bf16(sv, (B, Hkv, live, D))
+    plan = da.decode_attn_plan(B, Hq, Hkv, D, cap, cap, ragged=True)
+    assert B * Hkv >= plan.balanced_wgs * 4   # one run per wave
+    H.log(f"wave runs beyond 4 GiB: [{B}, {Hkv}, {cap}, {D}] caches, lengths 1..{live}")
+    dk, dv = nan_buffer((B, Hkv, cap, D)), nan_buffer((B, Hkv, cap, D))
+    dk[:, :, :live] = H.to_dev(k)
+    dv[:, :, :live] = H.to_dev(v)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device="cuda")
+    da.decode_attn_dense_ragged(plan, H.to_dev(q), dk, dv, out, SCALE, H.to_dev_i32(lens),
+                                workspace=da.workspace_for(plan))
+    torch.cuda.synchronize()
+    got = H.from_dev(out)
+    del dk, dv
+    release()
+    H.check_tolerance(got, oracle.dense_ragged(q, k, v, SCALE, lens, causal=True),
+                      "wave runs beyond 4 GiB")
 
 
 def test_paged_pool_beyond_4gib(da):

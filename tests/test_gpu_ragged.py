@@ -339,6 +339,7 @@ def test_length_order_boundaries(da, B, num_cus, Sq, ties):
     (24, 32, 8, 128, 2, 1, True),     # head tiles of 4 heads, paged
     (12, 16, 4, 64, 3, 16, False),    # 16 tokens: one head per stream, 16 rows, D = 64
     (30, 64, 1, 128, 2, 2, True),     # 64 heads on one kv head: 8 head tiles, paged
+    (20, 32, 4, 64, 2, 3, True),      # D = 64, 3 causal tokens, paged
 ])
 def test_wave_runs(da, B, Hq, Hkv, D, num_cus, Sq, paged):
     # at least as many streams as the grid has waves: every wave streams its own
