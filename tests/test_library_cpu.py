@@ -341,3 +341,22 @@ def test_read_probe_fails_closed(da):
     assert lib.decode_attn_read_probe(ctypes.c_void_p(0x10004), 1024, fake, None) == 1
     assert lib.decode_attn_read_probe(fake, 1000, fake, None) == 1
     assert lib.decode_attn_read_probe(fake, 0, fake, None) == 1
+
+
+def test_missing_library_fails_loudly():
+    # No fallback implementation: without the built library every entry point
+    # raises instead of computing anything another way.
+    import subprocess
+    import sys
+    code = ("import decode_attention_05_amd as d\n"
+            "d.library_path = '/nonexistent/libdecode_attn.so'\n"
+            "d._lib = None\n"
+            "try:\n"
+            "    d.decode_attn_plan(1, 8, 8, 64, 512, 300, num_cus=256)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "no fallback" in r.stdout
