@@ -195,6 +195,18 @@ def cpu_baseline(args, case, host, algo_bytes, W, threads=None, seconds=None):
     }
 
 
+def calibration_copy(torch):
+    """A plain 1 GiB device-to-device copy: its FETCH_SIZE / WRITE_SIZE counters
+    give the scale from counted to actual HBM bytes in the same process."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+    del src, dst
+
+
 def bench_selection(args, torch, np, da, W, H):
     """The on-device selection builder on the sparse workload's shapes ("select"),
     or builder + sparse attention as one step ("sparse_built"): 4 tokens, 65408
@@ -263,6 +275,8 @@ def bench_selection(args, torch, np, da, W, H):
         torch.cuda.synchronize()
         graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
         log(f"graph replay: {graph_us:.1f} us/step")
+    if args.calibrate_copy:
+        calibration_copy(torch)
     cpu = None
     if not args.no_cpu_baseline:
         from oracle.selection import build_selection
@@ -542,13 +556,7 @@ def main():
         del buf, sink
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
-        del src, dst
+        calibration_copy(torch)
 
     traffic = traffic_from_counters(args.workload + ("+step" if one_call else ""))
     result = {
