@@ -49,11 +49,15 @@ def log(msg):
     sys.stderr.flush()
 
 
-def kernel_source_hash() -> str:
+ATTENTION_SOURCES = ("kernels.hip", "device_common.h", "launch.h")
+SELECT_SOURCES = ("select.hip", "select.h")
+
+
+def kernel_source_hash(files=ATTENTION_SOURCES) -> str:
     """Hash of the kernel sources with comments and whitespace removed, so that
     stored counter readings stay valid across comment-only edits."""
     h = hashlib.sha256()
-    for fn in ("kernels.hip", "device_common.h", "launch.h"):
+    for fn in files:
         with open(os.path.join(ROOT, "decode_attention_05_amd", "csrc", fn)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -71,7 +75,8 @@ def traffic_from_counters(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+    files = SELECT_SOURCES if workload == "select" else ATTENTION_SOURCES
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -298,7 +303,7 @@ def bench_selection(args, torch, np, da, W, H):
         "roofline": {"bound": "hbm", "achieved": round(sel_bytes / (kern_us * 1e-6) / 1e9, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(sel_bytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
-                     "traffic": None, "kernel": "selection builder",
+                     "traffic": traffic_from_counters("select"), "kernel": "selection builder",
                      "kernel_us_mean": round(kern_us, 3), "kernel_launches_timed": len(kern_ms),
                      "bytes_per_launch": sel_bytes},
         "cpu_baseline": cpu,
