@@ -831,10 +831,11 @@ __device__ __forceinline__ void run_pieces(const PartialLaunch& a, unsigned char
 
 // LDS bytes per wave that hold finished pieces of a run until the run ends. A
 // record is a 16-byte header (first query row, flags, record bytes) and then
-// either the bf16 output rows [RT][D] of a whole stream or the fp32 partial
-// rows [RT][D] followed by (m, l) per row; the largest (16 partial rows at
-// D = 128) fits. Four waves' buffers and V tiles take 80 KiB at D = 128, so
-// two workgroups share a CU's 160 KiB.
+// either the bf16 output rows of a whole stream or the fp32 partial rows
+// followed by (m, l) per row, the rows padded (rows a multiple of 256 bytes
+// apart would put every row's lanes on the same LDS banks); the largest (16
+// partial rows at D = 128) fits. Four waves' buffers and V tiles
+// take 80 KiB at D = 128, so two workgroups share a CU's 160 KiB.
 constexpr int kPieceBufBytes = 12288;
 
 // Per-tile facts of the wave streamer (uniform across the wave).
@@ -1040,8 +1041,11 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
   // Records of finished pieces held in pb (pb_used bytes), written out by
   // flush: bf16 rows for a whole stream, else the fp32 partial with its (m, l)
   // in the run's slot.
-  const int direct_bytes = 16 + RT * D * 2;
-  const int partial_bytes = (16 + RT * D * 4 + RT * 8 + 15) & ~15;  // headers 16-byte aligned
+  // Record rows padded so that the rows of one write instruction fall on
+  // distinct LDS banks (for up to 8 bf16 or 4 fp32 rows).
+  constexpr int kDirRow = D * 2 + 32, kPartRow = D * 4 + 64;
+  const int direct_bytes = 16 + RT * kDirRow;
+  const int partial_bytes = (16 + RT * kPartRow + RT * 8 + 15) & ~15;  // headers 16-byte aligned
   int pb_used = 0;
   auto flush = [&]() {
     const int lane = fresh_lane();
@@ -1055,14 +1059,14 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
       at += __builtin_amdgcn_readfirstlane(h.z);
       if (r16 < RT) {
         if (fl & kTileDirect) {
-          const uint2* src = reinterpret_cast<const uint2*>(rec + 16) + (r16 * D + 4 * g) / 4;
+          const uint2* src = reinterpret_cast<const uint2*>(rec + 16 + r16 * kDirRow + 8 * g);
           uint16_t* dst = a.out + ((int64_t)row0 + r16) * D + 4 * g;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
             *reinterpret_cast<uint2*>(dst + 16 * dt) = src[4 * dt];
         } else {
-          const float4* src = reinterpret_cast<const float4*>(rec + 16) + (r16 * D + 4 * g) / 4;
-          const float2 ml = *reinterpret_cast<const float2*>(rec + 16 + RT * D * 4 + r16 * 8);
+          const float4* src = reinterpret_cast<const float4*>(rec + 16 + r16 * kPartRow + 16 * g);
+          const float2 ml = *reinterpret_cast<const float2*>(rec + 16 + RT * kPartRow + r16 * 8);
           const int64_t slot = (run * 2 + ((fl & kTileSlot1) ? 1 : 0)) * RT + r16;
           float* po = a.part_o + slot * D + 4 * g;
 #pragma unroll
@@ -1107,18 +1111,18 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
       if (r16 < RT) {
         if (direct) {
           const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-          uint2* dst = reinterpret_cast<uint2*>(rec + 16) + (r16 * D + 4 * g) / 4;
+          uint2* dst = reinterpret_cast<uint2*>(rec + 16 + r16 * kDirRow + 8 * g);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
             dst[4 * dt] = make_uint2(pack_bf16(O[dt][0] * inv, O[dt][1] * inv),
                                      pack_bf16(O[dt][2] * inv, O[dt][3] * inv));
         } else {
-          float4* dst = reinterpret_cast<float4*>(rec + 16) + (r16 * D + 4 * g) / 4;
+          float4* dst = reinterpret_cast<float4*>(rec + 16 + r16 * kPartRow + 16 * g);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
             dst[4 * dt] = make_float4(O[dt][0], O[dt][1], O[dt][2], O[dt][3]);
           if (g == 0)
-            *reinterpret_cast<float2*>(rec + 16 + RT * D * 4 + r16 * 8) = make_float2(m, lt);
+            *reinterpret_cast<float2*>(rec + 16 + RT * kPartRow + r16 * 8) = make_float2(m, lt);
         }
       }
       pb_used += bytes;
