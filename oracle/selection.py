@@ -23,14 +23,22 @@ Plain Python loops and ``sorted``: slow, obviously correct. Pinned by
 
 from __future__ import annotations
 
-import struct
-
 import numpy as np
 
 
-def total_order_key(x: float) -> int:
-    """Unsigned integer that orders binary32 values like IEEE 754 totalOrder."""
-    (u,) = struct.unpack("<I", struct.pack("<f", float(np.float32(x))))
+def total_order_key(x) -> int:
+    """Unsigned integer that orders binary32 values like IEEE 754 totalOrder.
+
+    ``x`` is a binary32 value (a numpy float32 scalar, whose bits are used as
+    they are) or its bit pattern as a Python int. totalOrder puts -NaN below
+    -inf and +NaN above +inf, orders NaNs of one sign by payload, and puts -0
+    below +0: on the bit pattern that is "flip every bit of a negative value,
+    set the sign bit of a non-negative one". The bits are never routed through
+    binary64, which would quiet a signaling NaN and change its payload."""
+    if isinstance(x, (int, np.integer)) and not isinstance(x, bool):
+        u = int(x) & 0xFFFFFFFF
+    else:
+        u = int(np.asarray(x, dtype=np.float32).reshape(()).view(np.uint32))
     return (u ^ 0xFFFFFFFF) if (u & 0x80000000) else (u | 0x80000000)
 
 
@@ -38,6 +46,7 @@ def build_selection(scores: np.ndarray, pos, n_idx: int, k_idx: int, window: int
                     win_base: int, topk: int) -> np.ndarray:
     """[B, topk] int32 selection for scores [B, >= n_idx] (float32) and positions [B]."""
     scores = np.asarray(scores, dtype=np.float32)
+    bits = scores.view(np.uint32)
     B = scores.shape[0]
     out = np.full((B, topk), -1, dtype=np.int32)
     for b in range(B):
@@ -49,7 +58,7 @@ def build_selection(scores: np.ndarray, pos, n_idx: int, k_idx: int, window: int
             position = p - n_win + 1 + j
             row.append(win_base + position % window)
         k = max(0, min(k_idx, n_idx, topk - n_win))
-        keys = [total_order_key(scores[b, i]) for i in range(n_idx)]
+        keys = [total_order_key(int(bits[b, i])) for i in range(n_idx)]
         ranked = sorted(range(n_idx), key=lambda i: (-keys[i], i))
         row.extend(sorted(ranked[:k]))
         out[b, :len(row)] = row

@@ -48,7 +48,18 @@ def scores_for(seed, B, n, kind="normal"):
         s[:, 1::89] = -np.inf
         s[:, 2::83] = 0.0
         s[:, 3::79] = -0.0
+        s = with_nan_payloads(s)
     return s.astype(np.float32)
+
+
+def with_nan_payloads(s):
+    """Quiet and signaling NaNs of both signs and several payloads (their order
+    under IEEE totalOrder is by sign, then payload bits)."""
+    bits = s.astype(np.float32).view(np.uint32).copy()
+    for start, step, pattern in ((4, 101, 0x7F800001), (6, 103, 0x7FBFFFFF), (8, 107, 0x7FC00001),
+                                 (9, 109, 0xFF800001), (10, 113, 0xFFFFFFFF)):
+        bits[:, start::step] = pattern
+    return bits.view(np.float32)
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "special"])
@@ -166,6 +177,7 @@ def draw_selection_case(i):
         s[:, 3::61] = -np.inf
         s[:, 5::67] = np.nan
         s[:, 7::71] = -0.0
+        s = with_nan_payloads(s)
     elif kind == "trend":
         s = (np.arange(n, dtype=np.float32) / n + 0.01 * s).astype(np.float32)
     elif kind == "constant":
