@@ -11,8 +11,15 @@ negative or lands outside ``[0, capacity)`` writes nothing.
 
 Several new rows per sequence (``append_rows``: the tokens of a pass are the
 last positions of the live prefix) and a paged cache written through a block
-table (``append_paged``; the metrale page "DflashScratch" writes its cache
-through slot indices) compose the same single-row write.
+table (``append_paged``) compose the same single-row write.
+
+``write_slots`` is the slot-addressed form of the metrale page "DflashScratch"
+(field slot_mapping_dev: one 64-bit paged-cache slot per token of the pass,
+consumed by a reshape-and-cache write): token n's rows go to slot s = page *
+page_size + row of the page pools. Readings: a negative slot is a padding
+token and writes nothing; a slot at or past num_pages * page_size writes
+nothing (a caller error, never written); two tokens naming one slot are a
+caller error (the oracle lets the later token win, the GPU gives one of them).
 
 Plain numpy indexing, one row at a time. Pinned by ``tests/test_append_oracle.py``.
 """
@@ -76,4 +83,25 @@ def append_paged(k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarr
                 continue
             k[pg, :, r % page_size, :] = k_new[b, :, t, :]
             v[pg, :, r % page_size, :] = v_new[b, :, t, :]
+    return k, v
+
+
+def write_slots(k_pages: np.ndarray, v_pages: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                slots):
+    """Return copies of the page pools [num_pages, Hkv, page_size, D] with token
+    n's rows k_rows[n] / v_rows[n] ([N, Hkv, D]) written at slot slots[n]: row
+    slots[n] % page_size of page slots[n] // page_size, for every kv head. A
+    negative slot or one past the pool writes nothing. One row at a time, in
+    token order."""
+    k = k_pages.copy()
+    v = v_pages.copy()
+    num_pages, Hkv, page_size, D = k.shape
+    for n in range(k_rows.shape[0]):
+        s = int(slots[n])
+        if s < 0 or s >= num_pages * page_size:
+            continue
+        page, row = s // page_size, s % page_size
+        for h in range(Hkv):
+            k[page, h, row, :] = k_rows[n, h, :]
+            v[page, h, row, :] = v_rows[n, h, :]
     return k, v

@@ -71,3 +71,67 @@ def test_paged_rows_follow_the_block_table():
     bad[0, 2] = 99
     kp2, _ = append_paged(to_pages(k), to_pages(v), bad, kn, vn, lens)
     assert np.array_equal(kp2[2], to_pages(k)[2])
+
+
+def test_slot_writes_closed_form():
+    from oracle.append import write_slots
+    num_pages, Hkv, page, D = 3, 2, 4, 8
+    _, k, v = W.random_case(98, num_pages, 2, Hkv, D, page)      # pools [3, 2, 4, 8]
+    sq, sk, sv, _ = W.seeds(99)
+    kr = W.normal_bf16(sk, (5, Hkv, D))
+    vr = W.normal_bf16(sv, (5, Hkv, D))
+    slots = np.array([5, -1, 0, 11, 12], np.int64)   # 12 = 3 pages * 4 rows: past the pool
+    k2, v2 = write_slots(k, v, kr, vr, slots)
+    placed = {(1, 1): 0, (0, 0): 2, (2, 3): 3}        # (page, row) -> token
+    for pg in range(num_pages):
+        for r in range(page):
+            n = placed.get((pg, r))
+            want_k = k[pg, :, r] if n is None else kr[n]
+            want_v = v[pg, :, r] if n is None else vr[n]
+            assert np.array_equal(k2[pg, :, r], want_k) and np.array_equal(v2[pg, :, r], want_v)
+
+
+def test_slot_writes_equal_the_block_table_writes():
+    from oracle.append import append_paged, write_slots
+    B, Hkv, page, max_pages, D, Sq = 3, 2, 4, 3, 8, 2
+    num_pages = 10
+    _, k, v = W.random_case(100, num_pages, 2, Hkv, D, page)
+    sq, sk, sv, _ = W.seeds(101)
+    kn = W.normal_bf16(sk, (B, Hkv, Sq, D))
+    vn = W.normal_bf16(sv, (B, Hkv, Sq, D))
+    table = np.array([[7, 2, 9], [0, 5, -1], [3, 99, 4]], np.int32)   # 99: outside the pool
+    lens = [10, 1, 6]
+    want = append_paged(k, v, table, kn, vn, lens)
+    # the slot of token t of sequence b, written out from the table (-1 where
+    # append_paged writes nothing)
+    slots = []
+    for b in range(B):
+        for t in range(Sq):
+            r = lens[b] - Sq + t
+            pg = int(table[b, r // page]) if r >= 0 else -1
+            slots.append(pg * page + r % page if 0 <= pg < num_pages else -1)
+    rows_k = np.ascontiguousarray(kn.transpose(0, 2, 1, 3).reshape(B * Sq, Hkv, D))
+    rows_v = np.ascontiguousarray(vn.transpose(0, 2, 1, 3).reshape(B * Sq, Hkv, D))
+    got = write_slots(k, v, rows_k, rows_v, np.array(slots, np.int64))
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_slot_writes_into_a_contiguous_cache():
+    # a contiguous cache [B, Hkv, capacity, D] is a pool of B pages of `capacity`
+    # rows: slot b * capacity + pos is the single-row append at pos
+    from oracle.append import write_slots
+    _, k, v = W.random_case(102, 3, 2, 2, 8, 10)
+    _, kn, vn = W.random_case(103, 3, 2, 2, 8, 1)
+    pos = [4, 0, 9]
+    want = append_kv(k, v, kn, vn, pos)
+    slots = np.array([b * 10 + p for b, p in enumerate(pos)], np.int64)
+    got = write_slots(k, v, kn[:, :, 0], vn[:, :, 0], slots)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_slot_writes_of_no_tokens_change_nothing():
+    from oracle.append import write_slots
+    _, k, v = W.random_case(104, 2, 2, 2, 8, 4)
+    got = write_slots(k, v, np.zeros((0, 2, 8), np.uint16), np.zeros((0, 2, 8), np.uint16),
+                      np.zeros(0, np.int64))
+    assert np.array_equal(got[0], k) and np.array_equal(got[1], v)
