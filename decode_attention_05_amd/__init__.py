@@ -22,6 +22,7 @@ __all__ = [
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_dense_ragged",
     "decode_attn_dense_paged", "decode_attn_dense_step", "decode_attn_sparse",
     "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
+    "decode_attn_write_slots", "SlotProblem",
     "decode_attn_set_timing_events", "decode_attn_read_probe", "decode_attn_status_str",
     "decode_attn_last_error",
     "workspace_for",
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_
                     "decode_attn_dense_ragged", "decode_attn_dense_paged", "decode_attn_dense_step",
                     "decode_attn_read_probe",
                     "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
+                    "decode_attn_write_slots",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
 
@@ -88,6 +90,14 @@ class AppendProblem(ctypes.Structure):
     ]
 
 
+class SlotProblem(ctypes.Structure):
+    """Mirror of ``decode_attn_slot_problem``."""
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+    ]
+
+
 class DecodeAttnError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -135,6 +145,8 @@ def library():
         lib.decode_attn_build_selection.restype = ctypes.c_int
         lib.decode_attn_append_kv.argtypes = [ctypes.POINTER(AppendProblem), P, P, P, P, P, P]
         lib.decode_attn_append_kv.restype = ctypes.c_int
+        lib.decode_attn_write_slots.argtypes = [ctypes.POINTER(SlotProblem), P, P, P, P, P, P]
+        lib.decode_attn_write_slots.restype = ctypes.c_int
         lib.decode_attn_set_timing_events.argtypes = [P, P]
         lib.decode_attn_set_timing_events.restype = ctypes.c_int
         lib.decode_attn_status_str.argtypes = [ctypes.c_int]
@@ -437,3 +449,22 @@ def decode_attn_append_kv(k_cache, v_cache, k_new, v_new, pos, window: int = 0, 
             _tensor_ptr(pos, "pos", (B,), torch.int32))
     return _run(library().decode_attn_append_kv, (ctypes.byref(prob), *args, _stream_ptr(stream)),
                 (k_cache, v_cache), prepare, (prob, k_cache, v_cache, k_new, v_new, pos))
+
+
+def decode_attn_write_slots(k_pages, v_pages, k_rows, v_rows, slot_mapping, stream=None,
+                            prepare=False):
+    """Write token n's rows k_rows/v_rows [N, Hkv, D] at slot slot_mapping[n] (int64
+    device tensor [N]) of the page pools [num_pages, Hkv, page_size, D]: row
+    slot % page_size of page slot // page_size; negative slots write nothing."""
+    import torch
+    num_pages, Hkv, page_size, D = k_pages.shape
+    N = k_rows.shape[0]
+    bf = torch.bfloat16
+    prob = SlotProblem(N, Hkv, D, page_size, num_pages)
+    args = (_tensor_ptr(k_pages, "k_pages", (num_pages, Hkv, page_size, D), bf),
+            _tensor_ptr(v_pages, "v_pages", (num_pages, Hkv, page_size, D), bf),
+            _tensor_ptr(k_rows, "k_rows", (N, Hkv, D), bf),
+            _tensor_ptr(v_rows, "v_rows", (N, Hkv, D), bf),
+            _tensor_ptr(slot_mapping, "slot_mapping", (N,), torch.int64))
+    return _run(library().decode_attn_write_slots, (ctypes.byref(prob), *args, _stream_ptr(stream)),
+                (k_pages, v_pages), prepare, (prob, k_pages, v_pages, k_rows, v_rows, slot_mapping))

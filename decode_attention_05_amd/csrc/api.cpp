@@ -1,8 +1,8 @@
 // api.cpp -- the C ABI of the decode-attention library: problem validation, the
 // split-K plan, and the entry points (dense with a host, device or per-sequence
 // length, paged, the one-call pass, sparse, the selection builder, the KV
-// append, and diagnostics). Host code only; the kernels live in kernels.hip,
-// select.hip, append.hip and probe.hip.
+// append, the slot-addressed KV write, and diagnostics). Host code only; the
+// kernels live in kernels.hip, select.hip, append.hip and probe.hip.
 //
 // The problem statement follows the fuel-dispatch page "DecodeFlashSpec"
 // (shapes of q, k, v; softmax_scale; k_len as the live prefix, counting the
@@ -628,6 +628,43 @@ decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, vo
   const hipError_t e = da::launch_append(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(DA_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+decode_attn_status decode_attn_write_slots(const decode_attn_slot_problem* p, void* k_pages,
+                                           void* v_pages, const void* k_rows, const void* v_rows,
+                                           const int64_t* slot_mapping, void* stream) {
+  if (!p) return fail(DA_ERR_INVALID_ARG, "problem pointer must be non-NULL");
+  if (p->num_tokens < 0 || p->num_kv_heads < 1 || p->page_size < 1 || p->num_pages < 1)
+    return fail(DA_ERR_INVALID_ARG,
+                "num_tokens must be >= 0; num_kv_heads, page_size and num_pages >= 1");
+  if (p->head_dim < 8 || p->head_dim > 512 || p->head_dim % 8 != 0)
+    return fail(DA_ERR_INVALID_ARG, "head_dim must be a multiple of 8 in [8, 512], got %d",
+                p->head_dim);
+  if ((double)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim > 9.0e15)
+    return fail(DA_ERR_INVALID_ARG, "page pools too large");
+  if ((int64_t)p->num_tokens * p->num_kv_heads * (p->head_dim / 8) * 2 > 0x7fffffffLL * 256)
+    return fail(DA_ERR_INVALID_ARG, "too many rows for one launch");
+  if (p->num_tokens == 0) return ok();  // nothing to write; no pointer is read
+  if (!k_pages || !v_pages || !k_rows || !v_rows || !slot_mapping)
+    return fail(DA_ERR_INVALID_ARG, "pools, rows and slot_mapping must be non-NULL");
+  if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_rows) || !aligned16(v_rows) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return fail(DA_ERR_INVALID_ARG, "pools and rows must be 16-byte aligned, slot_mapping 8-byte");
+  da::SlotWriteLaunch L{};
+  L.k_pages = static_cast<uint16_t*>(k_pages);
+  L.v_pages = static_cast<uint16_t*>(v_pages);
+  L.k_rows = static_cast<const uint16_t*>(k_rows);
+  L.v_rows = static_cast<const uint16_t*>(v_rows);
+  L.slots = slot_mapping;
+  L.N = p->num_tokens;
+  L.Hkv = p->num_kv_heads;
+  L.D = p->head_dim;
+  L.page_size = p->page_size;
+  L.num_pages = p->num_pages;
+  const hipError_t e = da::launch_write_slots(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "slot write kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

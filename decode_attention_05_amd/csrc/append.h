@@ -40,4 +40,19 @@ struct AppendRowsLaunch {
 
 hipError_t launch_append_rows(const AppendRowsLaunch& L, hipStream_t stream);
 
+// Slot-addressed rows: token n's rows go to row slots[n] % page_size of page
+// slots[n] / page_size of the pools; a negative slot or one past the pool is
+// skipped.
+struct SlotWriteLaunch {
+  uint16_t* k_pages;        // [num_pages, Hkv, page_size, D] bf16
+  uint16_t* v_pages;
+  const uint16_t* k_rows;   // [N, Hkv, D] bf16
+  const uint16_t* v_rows;
+  const int64_t* slots;     // [N] device slot indices
+  int N, Hkv, D, page_size;
+  int64_t num_pages;
+};
+
+hipError_t launch_write_slots(const SlotWriteLaunch& L, hipStream_t stream);
+
 }  // namespace da

@@ -12,6 +12,9 @@
 // One thread per 16-byte chunk of a (token, kv head, K or V) row. The rows of
 // a one-call decode pass (several new rows per sequence, at the end of its
 // live prefix read on the device, contiguous or paged) use append_rows_kernel.
+// write_slots_kernel writes rows to slots named one per token in device memory
+// (metrale page "DflashScratch", field slot_mapping_dev: 64-bit paged-cache
+// slot indices consumed by a reshape-and-cache write).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -74,7 +77,39 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendRowsLaunch a) {
   *dst = *src;
 }
 
+// One thread per 16-byte chunk of a (token, kv head, K or V) row. Slot s names
+// row s % page_size of page s / page_size; a negative slot (a padding token)
+// or a slot past the pool writes nothing.
+__global__ __launch_bounds__(256) void write_slots_kernel(SlotWriteLaunch a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int chunks = a.D / 8;
+  const int64_t per_side = (int64_t)a.N * a.Hkv * chunks;
+  if (t >= 2 * per_side) return;
+  const int which = (int)(t / per_side);  // 0: K, 1: V
+  const int64_t r = t % per_side;          // (token, head, chunk)
+  const int c = (int)(r % chunks);
+  const int64_t nh = r / chunks;           // n * Hkv + h
+  const int64_t n = nh / a.Hkv;
+  const int h = (int)(nh % a.Hkv);
+  const int64_t slot = a.slots[n];
+  if (slot < 0 || slot / a.page_size >= a.num_pages) return;
+  const int64_t page = slot / a.page_size, row = slot % a.page_size;
+  const uint4* src = reinterpret_cast<const uint4*>(which ? a.v_rows : a.k_rows) + r;
+  uint4* dst = reinterpret_cast<uint4*>(which ? a.v_pages : a.k_pages) +
+               ((page * a.Hkv + h) * a.page_size + row) * chunks + c;
+  *dst = *src;
+}
+
 }  // namespace
+
+hipError_t launch_write_slots(const SlotWriteLaunch& L, hipStream_t stream) {
+  const int64_t total = 2 * (int64_t)L.N * L.Hkv * (L.D / 8);
+  const int64_t blocks = (total + 255) / 256;
+  if (total <= 0 || blocks > 0x7fffffff || L.D % 8 != 0 || L.page_size < 1 || L.num_pages < 1)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(write_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_rows(const AppendRowsLaunch& L, hipStream_t stream) {
   const int64_t total = 2 * (int64_t)L.B * L.Hkv * L.Sq * (L.D / 8);

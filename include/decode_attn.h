@@ -314,6 +314,37 @@ decode_attn_status decode_attn_append_kv(const decode_attn_append_problem* p, vo
                                          const int32_t* pos, void* stream);
 
 /*
+ * Slot-addressed KV write (metrale page "DflashScratch", field slot_mapping_dev:
+ * one 64-bit paged-cache slot index per token of the pass, consumed by a
+ * reshape-and-cache write into the paged cache). Host struct.
+ */
+typedef struct {
+  int32_t num_tokens;   /* N >= 0 rows to write (0: nothing is enqueued or read)   */
+  int32_t num_kv_heads; /* Hkv >= 1                                                */
+  int32_t head_dim;     /* D: a multiple of 8, at most 512                         */
+  int32_t page_size;    /* rows per page, >= 1                                     */
+  int64_t num_pages;    /* pages in each pool, >= 1                                */
+} decode_attn_slot_problem;
+
+/*
+ * k_pages, v_pages [num_pages, Hkv, page_size, D] bf16 (written): the page pools
+ * of decode_attn_dense_paged (a contiguous cache [B, Hkv, capacity, D] is the
+ * same layout with page_size = capacity and num_pages = B). k_rows, v_rows
+ * [N, Hkv, D] bf16: token n's key and value rows, head-major inside a token.
+ * slot_mapping [N] int64 (device): token n's rows go to row s % page_size of
+ * page s / page_size, s = slot_mapping[n], for every kv head. A negative slot
+ * (a padding token) writes nothing; a slot at or past num_pages * page_size is
+ * a caller error that writes nothing. Two tokens naming one slot are a caller
+ * error: one of them is written. Slot values are device-resident and not
+ * validated on the host. One kernel on `stream`, no allocation, capturable.
+ * Pools and rows 16-byte aligned, slot_mapping 8-byte aligned.
+ * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_HIP (launch).
+ */
+decode_attn_status decode_attn_write_slots(const decode_attn_slot_problem* p, void* k_pages,
+                                           void* v_pages, const void* k_rows, const void* v_rows,
+                                           const int64_t* slot_mapping, void* stream);
+
+/*
  * Diagnostics: time the split-K partial kernel (the kernel that streams K and V)
  * with caller-created HIP events. After this call, every compute call made on
  * the calling thread records `ev_before` on its stream immediately before

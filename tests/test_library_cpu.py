@@ -360,3 +360,26 @@ def test_missing_library_fails_loudly():
                        timeout=120)
     assert r.returncode == 0, r.stderr
     assert "raised:" in r.stdout and "no fallback" in r.stdout
+
+
+def test_write_slots_validation(da):
+    lib = da.library()
+    P = ctypes.c_void_p
+
+    def call(prob, k=0x10000, v=0x20000, kr=0x30000, vr=0x40000, sl=0x50000):
+        return lib.decode_attn_write_slots(ctypes.byref(prob), P(k), P(v), P(kr), P(vr), P(sl), None)
+
+    good = dict(num_tokens=4, num_kv_heads=2, head_dim=128, page_size=16, num_pages=8)
+    for field, bad in [("num_tokens", -1), ("num_kv_heads", 0), ("head_dim", 100),
+                       ("head_dim", 1024), ("page_size", 0), ("num_pages", 0)]:
+        kw = dict(good, **{field: bad})
+        assert call(da.SlotProblem(**kw)) == 1, field
+    prob = da.SlotProblem(**good)
+    assert call(prob, k=0) == 1                     # NULL pool
+    assert call(prob, kr=0x30008) == 1              # rows not 16-byte aligned
+    assert call(prob, sl=0x50004) == 1              # slots not 8-byte aligned
+    assert "aligned" in da.decode_attn_last_error()
+    assert lib.decode_attn_write_slots(None, None, None, None, None, None, None) == 1
+    # no tokens: nothing is enqueued and no pointer is read (NULLs accepted)
+    empty = da.SlotProblem(**dict(good, num_tokens=0))
+    assert lib.decode_attn_write_slots(ctypes.byref(empty), None, None, None, None, None, None) == 0
