@@ -335,7 +335,8 @@ typedef struct {
  * page s / page_size, s = slot_mapping[n], for every kv head. A negative slot
  * (a padding token) writes nothing; a slot at or past num_pages * page_size is
  * a caller error that writes nothing. Two tokens naming one slot are a caller
- * error: one of them is written. Slot values are device-resident and not
+ * error: each 16-byte piece of that slot's rows then holds the same piece of
+ * one of those tokens' rows. Slot values are device-resident and not
  * validated on the host. One kernel on `stream`, no allocation, capturable.
  * Pools and rows 16-byte aligned, slot_mapping 8-byte aligned.
  * Returns DA_OK, DA_ERR_INVALID_ARG or DA_ERR_HIP (launch).

@@ -19,7 +19,8 @@ consumed by a reshape-and-cache write): token n's rows go to slot s = page *
 page_size + row of the page pools. Readings: a negative slot is a padding
 token and writes nothing; a slot at or past num_pages * page_size writes
 nothing (a caller error, never written); two tokens naming one slot are a
-caller error (the oracle lets the later token win, the GPU gives one of them).
+caller error (the oracle lets the later token win; the GPU writes each 16-byte
+piece from one of them).
 
 Plain numpy indexing, one row at a time. Pinned by ``tests/test_append_oracle.py``.
 """

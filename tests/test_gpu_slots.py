@@ -83,21 +83,24 @@ def test_no_tokens_is_a_no_op(da):
     assert np.array_equal(H.from_dev(dkp).reshape(kp.shape), kp)
 
 
-def test_duplicate_slots_write_one_of_the_rows(da):
-    # two tokens naming one slot is a caller error; the slot then holds one of
-    # the two rows (whole, never a mix), and nothing else changes
+def test_duplicate_slots_write_pieces_of_those_rows(da):
+    # two tokens naming one slot is a caller error; every 16-byte piece of that
+    # slot's rows then holds the same piece of one of the two tokens' rows (the
+    # pieces are written independently), and nothing else changes
     _, kp, vp = W.random_case(713, 2, 1, 2, 128, 8)
     kr, vr = rows(714, 3, 2, 128)
     slots = np.array([3, 3, 10], np.int64)
     gk, gv = run_write(da, kp, vp, kr, vr, slots)
-    for h in range(2):
-        cand = [(kr[n, h], vr[n, h]) for n in (0, 1)]
-        assert any(np.array_equal(gk[0, h, 3], ck) and np.array_equal(gv[0, h, 3], cv)
-                   for ck, cv in cand)
+    for got, new in ((gk, kr), (gv, vr)):
+        for h in range(2):
+            for c in range(0, 128, 8):
+                piece = got[0, h, 3, c:c + 8]
+                assert any(np.array_equal(piece, new[n, h, c:c + 8]) for n in (0, 1)), (h, c)
     want = write_slots(kp, vp, kr[2:], vr[2:], slots[2:])
     mask = np.ones(8, bool)
     mask[3] = False
     assert np.array_equal(gk[:, :, mask], want[0][:, :, mask])
+    assert np.array_equal(gv[:, :, mask], want[1][:, :, mask])
     assert np.array_equal(gk[1], want[0][1]) and np.array_equal(gv[1], want[1][1])
 
 
