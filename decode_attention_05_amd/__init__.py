@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "DecodeAttnError", "Problem", "Plan", "library", "library_path",
-    "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen", "decode_attn_dense_ragged",
+    "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_static", "decode_attn_dense_devlen",
+    "decode_attn_dense_ragged",
     "decode_attn_dense_paged", "decode_attn_dense_step", "decode_attn_sparse",
     "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
     "decode_attn_write_slots", "SlotProblem",
@@ -34,7 +35,8 @@ library_path = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 
-EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_devlen",
+EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_static",
+                    "decode_attn_dense_devlen",
                     "decode_attn_dense_ragged", "decode_attn_dense_paged", "decode_attn_dense_step",
                     "decode_attn_read_probe",
                     "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
@@ -122,6 +124,9 @@ def library():
         lib.decode_attn_dense.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
                                           ctypes.c_int64, P, ctypes.c_size_t, P]
         lib.decode_attn_dense.restype = ctypes.c_int
+        lib.decode_attn_dense_static.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
+                                                 ctypes.c_int64, P]
+        lib.decode_attn_dense_static.restype = ctypes.c_int
         lib.decode_attn_dense_devlen.argtypes = [ctypes.POINTER(Plan), P, P, P, P, ctypes.c_float,
                                                  P, P, ctypes.c_size_t, P]
         lib.decode_attn_dense_devlen.restype = ctypes.c_int
@@ -295,6 +300,23 @@ def decode_attn_dense(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int
     return _run(library().decode_attn_dense,
                 (ctypes.byref(plan), *args, float(softmax_scale), int(k_len), ws, wsb,
                  _stream_ptr(stream)), out, prepare, (plan, q, k, v, out, workspace))
+
+
+def decode_attn_dense_static(plan: Plan, q, k, v, out, softmax_scale: float, k_len: int,
+                             stream=None, prepare=False):
+    """decode_attn_dense with the library's static device workspace (no caller
+    workspace; for callers that cannot allocate). Calls that overlap on one
+    device race."""
+    import torch
+    p = plan.prob
+    B, Hq, Hkv, D, cap = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.capacity
+    Sq = p.seq_q
+    bf = torch.bfloat16
+    args = (_tensor_ptr(q, "q", (B, Hq, Sq, D), bf), _tensor_ptr(k, "k", (B, Hkv, cap, D), bf),
+            _tensor_ptr(v, "v", (B, Hkv, cap, D), bf), _tensor_ptr(out, "out", (B, Hq, Sq, D), bf))
+    return _run(library().decode_attn_dense_static,
+                (ctypes.byref(plan), *args, float(softmax_scale), int(k_len), _stream_ptr(stream)),
+                out, prepare, (plan, q, k, v, out))
 
 
 def decode_attn_dense_devlen(plan: Plan, q, k, v, out, softmax_scale: float, k_len_dev,

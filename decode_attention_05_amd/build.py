@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdecode_attn.so")
-SOURCES = ["api.cpp", "kernels.hip", "select.hip", "append.hip", "probe.hip"]
+SOURCES = ["api.cpp", "kernels.hip", "select.hip", "append.hip", "probe.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every HIP translation unit; hipcc's

@@ -28,6 +28,7 @@
 #include "launch.h"
 #include "probe.h"
 #include "select.h"
+#include "static_scratch.h"
 
 namespace {
 
@@ -466,6 +467,25 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
     std::fprintf(stderr, "[decode_attn] dense k_len=%lld splits=%d chunk=%d\n", (long long)k_len, S,
                  chunk);
   return run(L, stream);
+}
+
+decode_attn_status decode_attn_dense_static(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, int64_t k_len, void* stream) {
+  if (!plan) return fail(DA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->workspace_bytes > da::kStaticScratchBytes)
+    return fail(DA_ERR_WORKSPACE,
+                "the plan needs %llu bytes of workspace; the static workspace holds %zu "
+                "(use decode_attn_dense with a caller-owned workspace)",
+                (unsigned long long)plan->workspace_bytes, da::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (plan->workspace_bytes > 0) {
+    const hipError_t e = da::static_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(DA_ERR_HIP, "looking up the static workspace failed: %s", hipGetErrorString(e));
+  }
+  return decode_attn_dense(plan, q, k, v, out, softmax_scale, k_len, ws,
+                           ws ? (size_t)da::kStaticScratchBytes : 0, stream);
 }
 
 decode_attn_status decode_attn_dense_devlen(const decode_attn_plan_t* plan, const void* q,

@@ -141,6 +141,22 @@ decode_attn_status decode_attn_dense(const decode_attn_plan_t* plan, const void*
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): decode_attn_dense with the split
+ * workspace taken from a library-owned static device array of 16 MiB per
+ * device (held until the process ends) instead of a caller-owned buffer.
+ * Arguments as decode_attn_dense, without workspace and workspace_bytes.
+ * Allocates nothing. Every call on one device shares that device's array, so
+ * calls that overlap on one device (other streams, other threads) race and
+ * must not be issued; the array's contents between calls do not matter.
+ * Returns as decode_attn_dense; DA_ERR_WORKSPACE when plan->workspace_bytes
+ * exceeds 16 MiB, DA_ERR_HIP if the array's device address cannot be found.
+ */
+decode_attn_status decode_attn_dense_static(const decode_attn_plan_t* plan, const void* q,
+                                            const void* k, const void* v, void* out,
+                                            float softmax_scale, int64_t k_len, void* stream);
+
+/*
  * Dense decode attention with the live length read on the device (plan-once
  * decode: DecodeFlashSpec's k_len as a symbol bound to the live length each
  * token, fuel-dispatch page "DecodeFlashSpec", field k_len). Same arguments
