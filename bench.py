@@ -12,9 +12,13 @@ with every input already resident in HBM. Prints ONE JSON line:
                sparse workloads: the gathered rows, the selection, q and out)
   roofline     the partial kernel (the one that streams K and V): algorithmic bytes
                per launch / its mean duration from HIP events recorded on its own
-               stream around each launch in the timed region, against 8 TB/s
+               stream around each launch of a separate sampling loop after the
+               timed region, against 8 TB/s; the whole call (partial kernel and
+               merge) is timed the same way and reported beside it
   cpu_baseline the fp64 oracle timed on this host's cores over a bounded sample of
                the same workload
+  all_configs  (default workload only) the same measurements for the other four
+               configurations: dense tiny, dense GQA, dense large batch, sparse
 
 Workloads are the seeded synthetic inputs of ``workloads.py``; the default is the
 long-context dense GQA workload (B=4, Hq=64, Hkv=8, D=128, k_len = capacity =
@@ -89,10 +93,10 @@ def per_wave_runs(plan, B, Hkv, G, Sq) -> bool:
     return B * Hkv * (G // heads) >= plan.balanced_wgs * 4
 
 
-def build_inputs(args, torch, W, H):
-    if args.workload in W.RAGGED_CASES:
-        case = W.RAGGED_CASES[args.workload]
-        log(f"generating {args.workload} inputs (seed {case.seed})")
+def build_inputs(workload, W):
+    if workload in W.RAGGED_CASES:
+        case = W.RAGGED_CASES[workload]
+        log(f"generating {workload} inputs (seed {case.seed})")
         if case.page_size:
             q, k, v, table, lens = W.paged_inputs(case)
             layout = (f"paged cache of {k.shape[0]} pages x {case.page_size} rows, "
@@ -110,9 +114,9 @@ def build_inputs(args, torch, W, H):
                    max_k_len=case.len_hi, total_k_len=int(lens.sum()), page_size=case.page_size,
                    seq_q=case.seq_q)
         return case, host, 2 * k.nbytes, desc, cfg, case.algorithmic_bytes()
-    if args.workload in W.DENSE_CASES:
-        case = W.DENSE_CASES[args.workload]
-        log(f"generating {args.workload} inputs (seed {case.seed})")
+    if workload in W.DENSE_CASES:
+        case = W.DENSE_CASES[workload]
+        log(f"generating {workload} inputs (seed {case.seed})")
         q, k, v = W.dense_inputs(case)
         host = dict(q=q, k=k, v=v, sel=None)
         kv_bytes_alloc = 2 * k.nbytes
@@ -121,8 +125,8 @@ def build_inputs(args, torch, W, H):
         cfg = dict(batch=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv, head_dim=case.D,
                    capacity=case.capacity, k_len=case.k_len)
         return case, host, kv_bytes_alloc, desc, cfg, case.algorithmic_bytes()
-    case = W.SPARSE_CASES[args.workload]
-    log(f"generating {args.workload} inputs (seed {case.seed})")
+    case = W.SPARSE_CASES[workload]
+    log(f"generating {workload} inputs (seed {case.seed})")
     q, k, v, sel = W.sparse_inputs(case)
     host = dict(q=q, k=k, v=v, sel=sel)
     desc = (f"{case.name}: index-selected sparse decode, B={case.B} Hq={case.Hq} Hkv={case.Hkv} "
@@ -212,7 +216,7 @@ def calibration_copy(torch):
     del src, dst
 
 
-def bench_selection(args, torch, np, da, W, H):
+def bench_selection(args, torch, np, da, W):
     """The on-device selection builder on the sparse workload's shapes ("select"),
     or builder + sparse attention as one step ("sparse_built"): 4 tokens, 65408
     scored index candidates, 1920 chosen, a 128-slot window ring, width 2048."""
@@ -230,7 +234,7 @@ def bench_selection(args, torch, np, da, W, H):
     if built:
         log("generating sparse inputs (seed 5)")
         q, k, v, _ = W.sparse_inputs(case)
-        dq, dk, dv = H.to_dev(q), H.to_dev(k), H.to_dev(v)
+        dq, dk, dv = W.to_dev(q), W.to_dev(k), W.to_dev(v)
         out = torch.empty((case.B, case.Hq, 1, case.D), dtype=torch.bfloat16, device="cuda")
         plan = da.decode_attn_plan(case.B, case.Hq, case.Hkv, case.D, case.rows,
                                    topk_max=case.topk, kv_batch=1)
@@ -311,78 +315,28 @@ def bench_selection(args, torch, np, da, W, H):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long",
-                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
-                             "paged", "verify", "wide", "select", "sparse_built"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--events-every", type=int, default=8,
-                    help="bracket the streaming kernel with HIP events on every Nth timed "
-                         "step (an event pair adds ~6 us to the step it is in)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the HIP-graph replay timing of the plan-once call")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--force-splits", type=int, default=0, help="dense split count (tuning)")
-    ap.add_argument("--force-chunk", type=int, default=0,
-                    help="keys (dense) or selection entries (sparse) per split (tuning)")
-    ap.add_argument("--with-append", action="store_true",
-                    help="dense: each step first appends the token's K/V rows at k_len - 1 "
-                         "(a whole decode step: append, then attend)")
-    ap.add_argument("--step", action="store_true",
-                    help="dense: each step is one decode_attn_dense_step call, which writes the "
-                         "pass's new K/V rows at the end of each prefix and attends (one kernel "
-                         "pair instead of append + attention)")
-    ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the streaming-read ceiling measurement (a 4 GiB read probe)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after timing, run one plain 1 GiB device-to-device copy (a reference "
-                         "dispatch of known traffic for hardware-counter runs)")
-    args = ap.parse_args()
+ALL_CONFIGS = ("tiny", "gqa", "batch", "sparse")   # reported beside the default workload
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported. Decode attention here shards with no exchange across (batch, kv head) "
-              "units, so the whole-job figure for N GPUs is N times the one-GPU figure at a "
-              "weak-scaled batch; run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import decode_attention_05_amd as da
-    import workloads as W
-    from tests import helpers as H
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    da.library()
-
-    if args.workload in ("select", "sparse_built"):
-        return bench_selection(args, torch, np, da, W, H)
-
-    case, host, kv_alloc, desc, cfg, algo_bytes = build_inputs(args, torch, W, H)
+def run_workload(args, workload, torch, np, da, W, *, steps, warmup, graph, ceiling, cpu):
+    """Time one workload: `steps` timed steps after `warmup`, then separate
+    sampling loops for the kernel durations; returns the JSON line's fields."""
+    case, host, kv_alloc, desc, cfg, algo_bytes = build_inputs(workload, W)
     sparse = host["sel"] is not None
     sets = 1 if kv_alloc >= 2 * MALL_BYTES else max(4, math.ceil(2 * MALL_BYTES / kv_alloc))
     log(f"copying to device ({sets} K/V set{'s' if sets > 1 else ''})")
-    dq = H.to_dev(host["q"])
-    dks = [H.to_dev(host["k"])]
-    dvs = [H.to_dev(host["v"])]
+    dq = W.to_dev(host["q"])
+    dks = [W.to_dev(host["k"])]
+    dvs = [W.to_dev(host["v"])]
     for _ in range(sets - 1):
         dks.append(dks[0].clone())
         dvs.append(dvs[0].clone())
-    dsel = H.to_dev_i32(host["sel"]) if sparse else None
+    dsel = W.to_dev_i32(host["sel"]) if sparse else None
     ragged = "lens" in host
     paged = ragged and host["table"] is not None
     if ragged:
-        dlens = H.to_dev_i32(host["lens"])
-        dtable = H.to_dev_i32(host["table"]) if paged else None
+        dlens = W.to_dev_i32(host["lens"])
+        dtable = W.to_dev_i32(host["table"]) if paged else None
     B, Hq, D = case.B, case.Hq, case.D
     out = torch.empty((B, Hq, getattr(case, "seq_q", 1), D), dtype=torch.bfloat16, device="cuda")
     if ragged:
@@ -409,15 +363,12 @@ def main():
 
     append = args.with_append and not sparse and not ragged
     one_call = args.step and not sparse
-    if args.step and sparse:
-        print("--step applies to the dense workloads", file=sys.stderr)
-        sys.exit(2)
     Sq = getattr(case, "seq_q", 1)
     if append or one_call:
         rng = np.random.Generator(np.random.PCG64(7))
         nshape = (B, case.Hkv, Sq if one_call else 1, D)
-        kn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
-        vn = H.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
+        kn = W.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
+        vn = W.to_dev(W.f32_to_bf16_bits(rng.standard_normal(nshape, np.float32)))
         algo_bytes += 2 * 2 * B * case.Hkv * nshape[2] * D * 2  # new rows read and written
     if append:
         pos_dev = torch.full((B,), case.k_len - 1, dtype=torch.int32, device="cuda")
@@ -455,35 +406,67 @@ def main():
         for call in prepared[i % sets]:
             call()
 
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
+    # The measured streaming-read ceiling: a plain read of 4 GiB with the same
+    # load style, timed with events on the current stream. It runs before the
+    # warmup, so the timed steps also start from a GPU that has been busy.
+    read_ceiling = None
+    keep_alive = None
+    if ceiling:
+        buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            da.decode_attn_read_probe(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            da.decode_attn_read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read_ceiling = buf.numel() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        log(f"streaming-read ceiling: {read_ceiling:.0f} GB/s")
+        # Kept until the workload is done: memory handed back to the driver is
+        # cleared in the background, which competes for HBM bandwidth (and the
+        # graph capture below empties torch's cache).
+        keep_alive = (buf, sink)
+
+    log(f"{workload}: warmup {warmup} steps")
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
+    log(f"{workload}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    # Kernel durations, in a sampling loop of their own after the timed region
+    # (an event pair adds a few us to the step it brackets): the partial kernel
+    # alone, with events the library records on its stream immediately around
+    # that launch, then the whole call (partial kernel and merge) with events on
+    # the same stream around the call.
     stream = torch.cuda.current_stream()
-    every = max(1, args.events_every)
-    timed = list(range(0, args.steps, every))   # timed steps whose kernel is bracketed
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in timed]
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in timed]
+    n_samp = max(20, args.kernel_samples)
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_samp)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_samp)]
     for e in ev_b + ev_a:      # create the underlying hipEvent_t before handing it over
         e.record(stream)
     torch.cuda.synchronize()
-
-    log(f"timing {args.steps} steps (kernel events on every {every}th)")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i % every == 0:
-            da.decode_attn_set_timing_events(ev_b[i // every].cuda_event, ev_a[i // every].cuda_event)
-        elif i % every == 1:
-            da.decode_attn_set_timing_events(None, None)
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    for j in range(n_samp):
+        da.decode_attn_set_timing_events(ev_b[j].cuda_event, ev_a[j].cuda_event)
+        step(j)
     da.decode_attn_set_timing_events(None, None)
-
-    kern_ms = np.array([ev_b[j].elapsed_time(ev_a[j]) for j in range(len(timed))])
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    torch.cuda.synchronize()
+    kern_ms = np.array([ev_b[j].elapsed_time(ev_a[j]) for j in range(n_samp)])
+    for j in range(n_samp):
+        ev_b[j].record(stream)
+        step(j)
+        ev_a[j].record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([ev_b[j].elapsed_time(ev_a[j]) for j in range(n_samp)])
 
     # Warm: workloads rotated over several K/V copies (to defeat the 256 MB
     # Infinity Cache) are also timed on one copy, the cache-resident case.
@@ -491,21 +474,23 @@ def main():
     if sets > 1:
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(0)
         torch.cuda.synchronize()
-        warm_us = (time.perf_counter() - w0) * 1e6 / args.steps
+        warm_us = (time.perf_counter() - w0) * 1e6 / steps
     value = algo_bytes / (ms_per_step * 1e-3) / 1e9
     kern_mean_s = float(kern_ms.mean()) * 1e-3
+    call_mean_s = float(call_ms.mean()) * 1e-3
     achieved = algo_bytes / kern_mean_s / 1e9
-    log(f"{ms_per_step * 1e3:.1f} us/step, partial kernel mean {kern_mean_s * 1e6:.1f} us "
-        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f})")
+    log(f"{workload}: {ms_per_step * 1e3:.1f} us/step, partial kernel mean {kern_mean_s * 1e6:.1f} us "
+        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f}), "
+        f"whole call {call_mean_s * 1e6:.1f} us, {n_samp} launches sampled")
 
     # Plan-once decode: the same step captured once in a HIP graph (dense: the call
     # that reads k_len from device memory) and replayed; one replay runs every K/V
     # set once.
     graph_us = None
-    if not args.no_graph:
+    if graph:
         klen_dev = torch.full((1,), 0 if (sparse or ragged) else case.k_len, dtype=torch.int32,
                               device="cuda")
 
@@ -525,52 +510,33 @@ def main():
 
         gstep(0)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             for i in range(sets):
                 gstep(i)
         for _ in range(3):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
-        reps = max(1, args.steps // sets)
+        reps = max(1, steps // sets)
         g0 = time.perf_counter()
         for _ in range(reps):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
         graph_us = (time.perf_counter() - g0) * 1e6 / (reps * sets)
-        log(f"graph replay: {graph_us:.1f} us/step")
-        del graph
-
-    # The measured streaming-read ceiling: a plain read of 4 GiB with the same
-    # load style, timed with events on the current stream.
-    ceiling = None
-    if not args.no_ceiling:
-        buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
-        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        for _ in range(3):
-            da.decode_attn_read_probe(buf, sink)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record()
-        for _ in range(reps):
-            da.decode_attn_read_probe(buf, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        ceiling = buf.numel() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
-        log(f"streaming-read ceiling: {ceiling:.0f} GB/s")
-        del buf, sink
+        log(f"{workload}: graph replay: {graph_us:.1f} us/step")
+        del g
 
     if args.calibrate_copy:
         calibration_copy(torch)
 
-    traffic = traffic_from_counters(args.workload + ("+step" if one_call else ""))
+    traffic = traffic_from_counters(workload + ("+step" if one_call else ""))
     result = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -589,8 +555,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
-            "frac_of_measured_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
+            "measured_read_ceiling": None if read_ceiling is None else round(read_ceiling, 1),
+            "frac_of_measured_ceiling": (None if read_ceiling is None
+                                         else round(achieved / read_ceiling, 4)),
             "traffic": traffic,
             "kernel": (("attend_balanced_waves (length-balanced runs of one wave each)"
                         if per_wave_runs(plan, B, case.Hkv, Hq // case.Hkv, Sq)
@@ -600,20 +567,117 @@ def main():
             "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 3),
             "kernel_us_p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
-            "kernel_launches_timed": len(kern_ms),
+            "kernel_launches_timed": int(len(kern_ms)),
+            "call_us_mean": round(call_mean_s * 1e6, 3),
+            "call_frac": round(algo_bytes / call_mean_s / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_launch": algo_bytes,
         },
         "cpu_baseline": None,
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "warm_us_per_step": None if warm_us is None else round(warm_us, 3),
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(args, case, host, algo_bytes, W)
-        if args.workload in ("tiny", "sparse"):
+        if workload in ("tiny", "sparse"):
             one = cpu_baseline(args, case, host, algo_bytes, W, threads=1,
                                seconds=args.cpu_seconds / 2)
             result["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "sample")}
+    del prepared, dks, dvs, dq, out, ws, keep_alive
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
+
+
+def config_summary(r):
+    """The per-configuration record of all_configs."""
+    rf = r["roofline"]
+    return {
+        "workload": r["config"]["workload"], "us_per_step": r["us_per_step"],
+        "frac_of_hbm_peak": r["frac_of_hbm_peak"], "graph_us_per_step": r["graph_us_per_step"],
+        "warm_us_per_step": r["warm_us_per_step"], "kernel_us_mean": rf["kernel_us_mean"],
+        "kernel_frac": rf["frac"], "call_us_mean": rf["call_us_mean"],
+        "call_frac": rf["call_frac"], "traffic": rf["traffic"],
+        "algorithmic_bytes_per_step": r["config"]["algorithmic_bytes_per_step"],
+        "splits": r["config"]["splits"], "kv_sets": r["config"]["kv_sets"],
+        "steps": r["steps"], "kernel_launches_timed": rf["kernel_launches_timed"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
+                             "paged", "verify", "wide", "select", "sparse_built"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-samples", type=int, default=50,
+                    help="launches bracketed with HIP events after the timed region, for the "
+                         "kernel durations (at least 20)")
+    ap.add_argument("--events-every", type=int, default=8,
+                    help="selection workloads: bracket the builder on every Nth timed step")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing of the plan-once call")
+    ap.add_argument("--no-all-configs", action="store_true",
+                    help="default workload only: skip the other four configurations")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--force-splits", type=int, default=0, help="dense split count (tuning)")
+    ap.add_argument("--force-chunk", type=int, default=0,
+                    help="keys (dense) or selection entries (sparse) per split (tuning)")
+    ap.add_argument("--with-append", action="store_true",
+                    help="dense: each step first appends the token's K/V rows at k_len - 1 "
+                         "(a whole decode step: append, then attend)")
+    ap.add_argument("--step", action="store_true",
+                    help="dense: each step is one decode_attn_dense_step call, which writes the "
+                         "pass's new K/V rows at the end of each prefix and attends (one kernel "
+                         "pair instead of append + attention)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement (a 4 GiB read probe)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device-to-device copy (a reference "
+                         "dispatch of known traffic for hardware-counter runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported. Decode attention here shards with no exchange across (batch, kv head) "
+              "units, so the whole-job figure for N GPUs is N times the one-GPU figure at a "
+              "weak-scaled batch; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.step and args.workload in ("sparse", "sparse_mixed"):
+        print("--step applies to the dense workloads", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_05_amd as da
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    da.library()
+
+    if args.workload in ("select", "sparse_built"):
+        return bench_selection(args, torch, np, da, W)
+
+    result = run_workload(args, args.workload, torch, np, da, W, steps=args.steps,
+                          warmup=args.warmup, graph=not args.no_graph,
+                          ceiling=not args.no_ceiling, cpu=not args.no_cpu_baseline)
+    tuned = args.force_splits or args.force_chunk or args.with_append or args.step
+    if args.workload == "long" and not args.no_all_configs and not tuned:
+        # The other configurations: latency-bound ones get at least 200 timed steps.
+        result["all_configs"] = {}
+        for name in ALL_CONFIGS:
+            r = run_workload(args, name, torch, np, da, W, steps=max(args.steps, 200),
+                             warmup=max(args.warmup, 20), graph=not args.no_graph,
+                             ceiling=False, cpu=False)
+            result["all_configs"][name] = config_summary(r)
     print(json.dumps(result), flush=True)
 
 

@@ -32,20 +32,10 @@ def ensure_built():
         build.build()
 
 
-def to_dev(bits: np.ndarray):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
-
-
-def to_dev_i32(x: np.ndarray):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
-
-
-def from_dev(t) -> np.ndarray:
-    """Device bf16 tensor -> uint16 bit patterns on the host."""
-    import torch
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+# device transfer lives with the input generators (the benchmark uses it too)
+to_dev = W.to_dev
+to_dev_i32 = W.to_dev_i32
+from_dev = W.from_dev
 
 
 def as_f64(bits: np.ndarray) -> np.ndarray:

@@ -348,3 +348,23 @@ def repad(sel: np.ndarray, topk: int) -> np.ndarray:
     if keep < old and (sel[:, keep:] >= 0).any():
         raise ValueError("re-padding would drop valid entries")
     return out
+
+
+# --- device transfer of the drawn bits (torch only moves the bytes) ---------
+
+def to_dev(bits: np.ndarray):
+    """bfloat16 bit patterns (uint16) -> a bfloat16 device tensor with those bits."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev_i32(x: np.ndarray):
+    """int32 host array -> int32 device tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    """bfloat16 device tensor -> its bit patterns (uint16) on the host."""
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
