@@ -713,7 +713,11 @@ decode_attn_status decode_attn_set_timing_events(void* ev_before, void* ev_after
 }
 
 const char* decode_attn_status_str(decode_attn_status s) {
-  switch (s) {
+  // A C caller may pass any int; read it as one (a C++ load of an out-of-range
+  // enumeration value is undefined).
+  int v = 0;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case DA_OK: return "DA_OK";
     case DA_ERR_INVALID_ARG: return "DA_ERR_INVALID_ARG";
     case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED";
