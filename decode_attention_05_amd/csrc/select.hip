@@ -6,8 +6,8 @@
 // decode_body writes the window as a ring at pos % window):
 //   * the window rows of positions max(0, pos - W + 1) .. pos, oldest first,
 //     position p living in KV row win_base + p % W;
-//   * the k index candidates (0 .. n_idx - 1) with the largest scores, in
-//     descending score order, ties to the lower index, k = min(k_idx, n_idx,
+//   * the k index candidates (0 .. n_idx - 1) with the largest scores, listed
+//     in ascending row order, ties to the lower index, k = min(k_idx, n_idx,
 //     topk - window entries), scores ordered as IEEE 754 totalOrder;
 //   * -1 for the rest.
 // Building it on the device removes the host score download that keeps a step
