@@ -79,7 +79,7 @@ def traffic_from_counters(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    files = SELECT_SOURCES if workload == "select" else ATTENTION_SOURCES
+    files = SELECT_SOURCES if workload in ("select", "select_one") else ATTENTION_SOURCES
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return entry.get("hbm_bytes_per_launch")
@@ -217,9 +217,11 @@ def calibration_copy(torch):
 
 
 def bench_selection(args, torch, np, da, W):
-    """The on-device selection builder on the sparse workload's shapes ("select"),
-    or builder + sparse attention as one step ("sparse_built"): 4 tokens, 65408
-    scored index candidates, 1920 chosen, a 128-slot window ring, width 2048."""
+    """The on-device selection builder on the sparse workload's shapes ("select":
+    the split builder, several workgroups per token with a workspace;
+    "select_one": one workgroup per token), or split builder + sparse attention
+    as one step ("sparse_built"): 4 tokens, 65408 scored index candidates, 1920
+    chosen, a 128-slot window ring, width 2048."""
     case = W.SPARSE_CASES["sparse"]
     n_idx = case.rows - case.window
     k_idx = case.topk - case.window
@@ -231,6 +233,17 @@ def bench_selection(args, torch, np, da, W):
     dsel = torch.empty((case.B, case.topk), dtype=torch.int32, device="cuda")
     sel_bytes = scores.nbytes + pos.nbytes + case.B * case.topk * 4
     built = args.workload == "sparse_built"
+    one_wg = args.workload == "select_one"
+    sws_bytes = 0 if one_wg else da.decode_attn_select_workspace(case.B, n_idx, k_idx, case.window,
+                                                                 case.topk)
+    sws = torch.empty(sws_bytes, dtype=torch.uint8, device="cuda") if sws_bytes else None
+
+    def build_sel():
+        if one_wg:
+            da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
+        else:
+            da.decode_attn_build_selection_ws(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx,
+                                              sws)
     if built:
         log("generating sparse inputs (seed 5)")
         q, k, v, _ = W.sparse_inputs(case)
@@ -244,7 +257,7 @@ def bench_selection(args, torch, np, da, W):
         algo_bytes = sel_bytes
 
     def step():
-        da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
+        build_sel()
         if built:
             da.decode_attn_sparse(plan, dq, dk, dv, dsel, case.topk, out, case.scale, case.rows, ws)
 
@@ -260,7 +273,7 @@ def bench_selection(args, torch, np, da, W):
     for i in range(args.steps):
         if i % every == 0:
             ev_b[i // every].record(stream)
-        da.decode_attn_build_selection(dsc, dpos, dsel, n_idx, k_idx, case.window, n_idx)
+        build_sel()
         if i % every == 0:
             ev_a[i // every].record(stream)
         if built:
@@ -296,7 +309,9 @@ def bench_selection(args, torch, np, da, W):
                "cores": 1, "kind": "oracle",
                "sample": f"selection of 1 of {case.B} tokens, {per_token:.2f} s, scaled to {case.B}"}
     value = algo_bytes / (us * 1e-6) / 1e9
-    desc = ("selection builder" + (" + sparse attention" if built else "") +
+    desc = (("selection builder, one workgroup per token" if one_wg else
+             "selection builder, 16 workgroups per token and a merge") +
+            (" + sparse attention" if built else "") +
             f": B={case.B} candidates={n_idx} k={k_idx} window={case.window} topk={case.topk}")
     print(json.dumps({
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
@@ -307,7 +322,8 @@ def bench_selection(args, torch, np, da, W):
         "roofline": {"bound": "hbm", "achieved": round(sel_bytes / (kern_us * 1e-6) / 1e9, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(sel_bytes / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
-                     "traffic": traffic_from_counters("select"), "kernel": "selection builder",
+                     "traffic": traffic_from_counters(args.workload if not built else "select"),
+                     "kernel": "selection builder (all its kernels)",
                      "kernel_us_mean": round(kern_us, 3), "kernel_launches_timed": len(kern_ms),
                      "bytes_per_launch": sel_bytes},
         "cpu_baseline": cpu,
@@ -611,7 +627,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "gqa", "long", "batch", "sparse", "sparse_mixed", "ragged",
-                             "paged", "verify", "wide", "select", "sparse_built"])
+                             "paged", "verify", "wide", "select", "select_one", "sparse_built"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-samples", type=int, default=50,
                     help="launches bracketed with HIP events after the timed region, for the "
@@ -663,7 +679,7 @@ def main():
     torch.cuda.set_device(0)
     da.library()
 
-    if args.workload in ("select", "sparse_built"):
+    if args.workload in ("select", "select_one", "sparse_built"):
         return bench_selection(args, torch, np, da, W)
 
     result = run_workload(args, args.workload, torch, np, da, W, steps=args.steps,

@@ -22,7 +22,8 @@ __all__ = [
     "decode_attn_plan", "decode_attn_dense", "decode_attn_dense_static", "decode_attn_dense_devlen",
     "decode_attn_dense_ragged",
     "decode_attn_dense_paged", "decode_attn_dense_step", "decode_attn_sparse",
-    "decode_attn_build_selection", "SelectProblem", "decode_attn_append_kv", "AppendProblem",
+    "decode_attn_build_selection", "decode_attn_build_selection_ws", "decode_attn_select_workspace",
+    "SelectProblem", "decode_attn_append_kv", "AppendProblem",
     "decode_attn_write_slots", "SlotProblem",
     "decode_attn_set_timing_events", "decode_attn_read_probe", "decode_attn_status_str",
     "decode_attn_last_error",
@@ -39,7 +40,9 @@ EXPORTED_SYMBOLS = ("decode_attn_plan", "decode_attn_dense", "decode_attn_dense_
                     "decode_attn_dense_devlen",
                     "decode_attn_dense_ragged", "decode_attn_dense_paged", "decode_attn_dense_step",
                     "decode_attn_read_probe",
-                    "decode_attn_sparse", "decode_attn_build_selection", "decode_attn_append_kv",
+                    "decode_attn_sparse", "decode_attn_build_selection",
+                    "decode_attn_build_selection_ws", "decode_attn_select_workspace",
+                    "decode_attn_append_kv",
                     "decode_attn_write_slots",
                     "decode_attn_set_timing_events", "decode_attn_status_str",
                     "decode_attn_last_error")
@@ -148,6 +151,12 @@ def library():
         lib.decode_attn_sparse.restype = ctypes.c_int
         lib.decode_attn_build_selection.argtypes = [ctypes.POINTER(SelectProblem), P, P, P, P]
         lib.decode_attn_build_selection.restype = ctypes.c_int
+        lib.decode_attn_build_selection_ws.argtypes = [ctypes.POINTER(SelectProblem), P, P, P, P,
+                                                       ctypes.c_size_t, P]
+        lib.decode_attn_build_selection_ws.restype = ctypes.c_int
+        lib.decode_attn_select_workspace.argtypes = [ctypes.POINTER(SelectProblem),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        lib.decode_attn_select_workspace.restype = ctypes.c_int
         lib.decode_attn_append_kv.argtypes = [ctypes.POINTER(AppendProblem), P, P, P, P, P, P]
         lib.decode_attn_append_kv.restype = ctypes.c_int
         lib.decode_attn_write_slots.argtypes = [ctypes.POINTER(SlotProblem), P, P, P, P, P, P]
@@ -439,6 +448,12 @@ def decode_attn_sparse(plan: Plan, q, k, v, sel, topk: int, out, softmax_scale: 
                 prepare, (plan, q, k, v, sel, out, workspace))
 
 
+def _select_problem(scores, sel, n_idx, k_idx, window, win_base):
+    B, topk = sel.shape
+    return SelectProblem(B, int(n_idx), int(scores.shape[1]), int(k_idx), int(window),
+                         int(win_base), int(topk))
+
+
 def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window: int,
                                 win_base: int, stream=None, prepare=False):
     """Fill ``sel`` [B, topk] int32 on the device: window ring rows, then the k_idx
@@ -446,14 +461,47 @@ def decode_attn_build_selection(scores, pos, sel, n_idx: int, k_idx: int, window
     import torch
     B, topk = sel.shape
     stride = scores.shape[1]
-    prob = SelectProblem(B, int(n_idx), int(stride), int(k_idx), int(window), int(win_base),
-                         int(topk))
+    prob = _select_problem(scores, sel, n_idx, k_idx, window, win_base)
     sp = _tensor_ptr(scores, "scores", (B, stride), torch.float32)
     pp = _tensor_ptr(pos, "pos", (B,), torch.int32)
     selp = _tensor_ptr(sel, "sel", (B, topk), torch.int32)
     return _run(library().decode_attn_build_selection,
                 (ctypes.byref(prob), sp, pp, selp, _stream_ptr(stream)), sel, prepare,
                 (prob, scores, pos, sel))
+
+
+def decode_attn_select_workspace(batch: int, n_idx: int, k_idx: int, window: int, topk: int,
+                                 score_stride: int | None = None) -> int:
+    """Workspace bytes of decode_attn_build_selection_ws for this shape (host only)."""
+    stride = n_idx + (-n_idx) % 4 if score_stride is None else score_stride
+    prob = SelectProblem(int(batch), int(n_idx), int(max(stride, 4)), int(k_idx), int(window), 0,
+                         int(topk))
+    n = ctypes.c_size_t(0)
+    _check(library().decode_attn_select_workspace(ctypes.byref(prob), ctypes.byref(n)))
+    return int(n.value)
+
+
+def decode_attn_build_selection_ws(scores, pos, sel, n_idx: int, k_idx: int, window: int,
+                                   win_base: int, workspace=None, stream=None, prepare=False):
+    """decode_attn_build_selection with several workgroups per token and a
+    caller-owned device workspace of decode_attn_select_workspace bytes."""
+    import torch
+    B, topk = sel.shape
+    stride = scores.shape[1]
+    prob = _select_problem(scores, sel, n_idx, k_idx, window, win_base)
+    sp = _tensor_ptr(scores, "scores", (B, stride), torch.float32)
+    pp = _tensor_ptr(pos, "pos", (B,), torch.int32)
+    selp = _tensor_ptr(sel, "sel", (B, topk), torch.int32)
+    if workspace is None:
+        ws, wsb = None, 0
+    else:
+        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
+                and workspace.is_contiguous()):
+            raise TypeError("workspace must be a contiguous device tensor")
+        ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return _run(library().decode_attn_build_selection_ws,
+                (ctypes.byref(prob), sp, pp, selp, ws, wsb, _stream_ptr(stream)), sel, prepare,
+                (prob, scores, pos, sel, workspace))
 
 
 def decode_attn_append_kv(k_cache, v_cache, k_new, v_new, pos, window: int = 0, win_base: int = 0,

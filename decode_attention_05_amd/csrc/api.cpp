@@ -377,6 +377,45 @@ decode_attn_status dense_with_lengths(const decode_attn_plan_t* plan, const void
   return ok();
 }
 
+decode_attn_status select_launch(const decode_attn_select_problem* p, const float* scores,
+                                 const int32_t* pos, int32_t* sel, da::SelectLaunch* L) {
+  if (!p) return fail(DA_ERR_INVALID_ARG, "problem pointer must be non-NULL");
+  if (p->batch < 1 || p->topk < 1 || p->n_idx < 0 || p->window < 0 || p->k_idx < 0)
+    return fail(DA_ERR_INVALID_ARG, "batch and topk must be >= 1; n_idx, window, k_idx >= 0");
+  if (p->k_idx > da::kSelectMaxK)
+    return fail(DA_ERR_INVALID_ARG, "k_idx must be <= %d, got %d", da::kSelectMaxK, p->k_idx);
+  if (p->n_idx > da::kSelectMaxCandidates)
+    return fail(DA_ERR_UNSUPPORTED, "n_idx: at most %d index candidates per token, got %d",
+                da::kSelectMaxCandidates, p->n_idx);
+  if (p->score_stride < p->n_idx || p->score_stride < 1)
+    return fail(DA_ERR_INVALID_ARG, "score_stride must be >= max(n_idx, 1)");
+  if (p->win_base < 0 || p->win_base + p->window > 0x7fffffffLL)
+    return fail(DA_ERR_INVALID_ARG, "window rows must lie in [0, 2^31)");
+  if (p->n_idx > 0x7fffffff - 1 || (int64_t)p->batch * p->topk > 0x7fffffffLL)
+    return fail(DA_ERR_INVALID_ARG, "selection too large");
+  if (!pos || !sel) return fail(DA_ERR_INVALID_ARG, "pos and sel must be non-NULL");
+  if (((uintptr_t)pos & 3u) || ((uintptr_t)sel & 3u))
+    return fail(DA_ERR_INVALID_ARG, "pos and sel must be 4-byte aligned");
+  if (p->k_idx > 0 && p->n_idx > 0) {
+    if (!scores) return fail(DA_ERR_INVALID_ARG, "scores must be non-NULL when k_idx > 0");
+    if (((uintptr_t)scores & 15u) || (p->score_stride & 3))
+      return fail(DA_ERR_INVALID_ARG,
+                  "scores must be 16-byte aligned with a row stride that is a multiple of 4");
+  }
+  *L = da::SelectLaunch{};
+  L->scores = scores;
+  L->score_stride = p->score_stride;
+  L->pos = pos;
+  L->sel = sel;
+  L->B = p->batch;
+  L->n_idx = p->n_idx;
+  L->k_idx = p->k_idx;
+  L->window = p->window;
+  L->topk = p->topk;
+  L->win_base = p->win_base;
+  return DA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -576,41 +615,49 @@ decode_attn_status decode_attn_sparse(const decode_attn_plan_t* plan, const void
 decode_attn_status decode_attn_build_selection(const decode_attn_select_problem* p,
                                                const float* scores, const int32_t* pos,
                                                int32_t* sel, void* stream) {
-  if (!p) return fail(DA_ERR_INVALID_ARG, "problem pointer must be non-NULL");
-  if (p->batch < 1 || p->topk < 1 || p->n_idx < 0 || p->window < 0 || p->k_idx < 0)
-    return fail(DA_ERR_INVALID_ARG, "batch and topk must be >= 1; n_idx, window, k_idx >= 0");
-  if (p->k_idx > da::kSelectMaxK)
-    return fail(DA_ERR_INVALID_ARG, "k_idx must be <= %d, got %d", da::kSelectMaxK, p->k_idx);
-  if (p->n_idx > da::kSelectMaxCandidates)
-    return fail(DA_ERR_UNSUPPORTED, "n_idx: at most %d index candidates per token, got %d",
-                da::kSelectMaxCandidates, p->n_idx);
-  if (p->score_stride < p->n_idx || p->score_stride < 1)
-    return fail(DA_ERR_INVALID_ARG, "score_stride must be >= max(n_idx, 1)");
-  if (p->win_base < 0 || p->win_base + p->window > 0x7fffffffLL)
-    return fail(DA_ERR_INVALID_ARG, "window rows must lie in [0, 2^31)");
-  if (p->n_idx > 0x7fffffff - 1 || (int64_t)p->batch * p->topk > 0x7fffffffLL)
-    return fail(DA_ERR_INVALID_ARG, "selection too large");
-  if (!pos || !sel) return fail(DA_ERR_INVALID_ARG, "pos and sel must be non-NULL");
-  if (((uintptr_t)pos & 3u) || ((uintptr_t)sel & 3u))
-    return fail(DA_ERR_INVALID_ARG, "pos and sel must be 4-byte aligned");
-  if (p->k_idx > 0 && p->n_idx > 0) {
-    if (!scores) return fail(DA_ERR_INVALID_ARG, "scores must be non-NULL when k_idx > 0");
-    if (((uintptr_t)scores & 15u) || (p->score_stride & 3))
-      return fail(DA_ERR_INVALID_ARG,
-                  "scores must be 16-byte aligned with a row stride that is a multiple of 4");
-  }
-  da::SelectLaunch L{};
-  L.scores = scores;
-  L.score_stride = p->score_stride;
-  L.pos = pos;
-  L.sel = sel;
-  L.B = p->batch;
-  L.n_idx = p->n_idx;
-  L.k_idx = p->k_idx;
-  L.window = p->window;
-  L.topk = p->topk;
-  L.win_base = p->win_base;
+  da::SelectLaunch L;
+  const decode_attn_status s = select_launch(p, scores, pos, sel, &L);
+  if (s != DA_OK) return s;
   const hipError_t e = da::launch_select(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(DA_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+decode_attn_status decode_attn_select_workspace(const decode_attn_select_problem* p,
+                                                size_t* bytes) {
+  if (!bytes) return fail(DA_ERR_INVALID_ARG, "bytes must be non-NULL");
+  da::SelectLaunch L;
+  // pointers are not needed for the size: validate the shape only
+  static const int32_t dummy[4] = {0, 0, 0, 0};
+  alignas(16) static const float dummy_scores[4] = {0.f, 0.f, 0.f, 0.f};
+  const decode_attn_status s =
+      select_launch(p, dummy_scores, dummy, const_cast<int32_t*>(dummy), &L);
+  if (s != DA_OK) return s;
+  *bytes = da::select_workspace_bytes(p->batch, p->n_idx);
+  return ok();
+}
+
+decode_attn_status decode_attn_build_selection_ws(const decode_attn_select_problem* p,
+                                                  const float* scores, const int32_t* pos,
+                                                  int32_t* sel, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  da::SelectLaunch L;
+  const decode_attn_status s = select_launch(p, scores, pos, sel, &L);
+  if (s != DA_OK) return s;
+  const size_t need = da::select_workspace_bytes(p->batch, p->n_idx);
+  if (need > 0) {
+    if (!workspace)
+      return fail(DA_ERR_WORKSPACE, "workspace is NULL but the selection needs %zu bytes", need);
+    if (workspace_bytes < need)
+      return fail(DA_ERR_WORKSPACE, "workspace has %zu bytes, the selection needs %zu",
+                  workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(DA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  L.ws = need > 0 ? workspace : nullptr;
+  L.parts = need > 0 ? da::select_parts(p->n_idx) : 0;
+  const hipError_t e = need > 0 ? da::launch_select_split(L, static_cast<hipStream_t>(stream))
+                                : da::launch_select(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(DA_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -136,6 +136,19 @@ __device__ __forceinline__ void for_each_key(const float* sc, int n, Fn fn) {
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips): within each row of 16 lanes by shifts
+// of 1, 2, 4 and 8, then the rows' totals carried into the following rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return x;
+}
+
 // Digit histogram (bits shift .. shift+7) of the keys matching prefix under mask,
 // then choice of the digit that holds the need-th largest matching key.
 // Updates prefix/mask/need; returns the count of keys in the chosen digit.
@@ -167,13 +180,8 @@ __device__ uint32_t radix_pass(Visit&& visit, int shift, uint32_t& prefix, uint3
       for (int g = 0; g < kCopies; ++g) c[j] += S.hist[g][4 * tid + j];
     }
     const uint32_t t = c[0] + c[1] + c[2] + c[3];
-    uint32_t x = t;  // inclusive suffix over lanes: digits >= 4 * tid
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_down(x, off);
-      if (tid + off < 64) x += y;
-    }
-    uint32_t above = x - t;  // keys with digit >= 4 * (tid + 1)
+    const uint32_t incl_lo = wave_incl_scan(t);  // digits < 4 * (tid + 1)
+    uint32_t above = __builtin_amdgcn_readlane(incl_lo, 63) - incl_lo;  // digits >= 4 * (tid + 1)
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
       const uint32_t incl = above + c[j];
@@ -196,12 +204,7 @@ __device__ uint32_t radix_pass(Visit&& visit, int shift, uint32_t& prefix, uint3
 // wave totals through LDS); *total receives the block sum.
 __device__ uint32_t block_exclusive_scan(uint32_t v, Shared& S, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) S.wsum[wave] = x;
   __syncthreads();
   uint32_t base = 0u, tot = 0u;
@@ -337,21 +340,30 @@ __device__ void exact_select(Visit&& visit, int k, int nwords, Shared& S) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaunch a) {
-  __shared__ Shared S;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* sc = a.scores + (int64_t)b * a.score_stride;
-  int32_t* out = a.sel + (int64_t)b * a.topk;
-
-  const int pos = a.pos[b];
+// Window entries of token b (n_win) and the size k of its index part.
+__device__ __forceinline__ void token_counts(const SelectLaunch& a, int pos, int* n_win_out,
+                                             int* k_out) {
   int n_win = 0;
   if (a.window > 0 && pos >= 0) n_win = pos + 1 < a.window ? pos + 1 : a.window;
   if (n_win > a.topk) n_win = a.topk;
   int k = a.k_idx < a.n_idx ? a.k_idx : a.n_idx;
   if (k > a.topk - n_win) k = a.topk - n_win;
   if (k < 0) k = 0;
-  for (int j = tid; j < a.topk; j += kSelThreads) {
+  *n_win_out = n_win;
+  *k_out = k;
+}
+
+// Row b of the selection around its index part: the window rows, oldest
+// first, then -1 after the n_win + k entries. Every thread of the workgroup
+// calls it; returns n_win and k.
+__device__ __forceinline__ void window_and_pads(const SelectLaunch& a, int b, int nthreads,
+                                                int* n_win_out, int* k_out) {
+  const int tid = threadIdx.x;
+  int32_t* out = a.sel + (int64_t)b * a.topk;
+  const int pos = a.pos[b];
+  int n_win, k;
+  token_counts(a, pos, &n_win, &k);
+  for (int j = tid; j < a.topk; j += nthreads) {
     if (j < n_win) {
       const int p = pos - n_win + 1 + j;  // >= 0
       out[j] = (int32_t)(a.win_base + p % a.window);
@@ -359,8 +371,14 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
       out[j] = -1;
     }
   }
-  if (k == 0) return;
-  const int n = a.n_idx;
+  *n_win_out = n_win;
+  *k_out = k;
+}
+
+// The index part of one token with one workgroup: the k (>= 1) best of the n
+// scores of row `sc`, in ascending row order, into dst[0, k).
+__device__ __forceinline__ void index_part(const float* sc, int n, int k, int32_t* dst, Shared& S) {
+  const int tid = threadIdx.x;
   const int nwords = (n + 31) >> 5;
 
   // 1. Prefilter (rows >= kPreMinN): a sample of the keys gives a lower bound
@@ -408,15 +426,10 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
         for (int u = 0; u < kLoads; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e) cnt += (c.valid[u] && c.key[u][e] >= L0) ? 1u : 0u;
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
+        const uint32_t incl = wave_incl_scan(cnt);
         uint32_t base = 0u;
         if (lane == 63) base = atomicAdd(&S.n_pre, incl);
-        uint32_t pos = __shfl(base, 63) + incl - cnt;
+        uint32_t pos = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
           const uint32_t i0 = 4u * (uint32_t)(vbase + tid + kSelThreads * u);
@@ -465,7 +478,6 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
   for (int w = w0; w < w1; ++w) cnt += __popc(S.bitmap[w]);
   uint32_t tot;
   uint32_t off = block_exclusive_scan(cnt, S, &tot);
-  int32_t* dst = out + n_win;
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = S.bitmap[w];
     while (bits) {
@@ -476,11 +488,369 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaunch a) {
+  __shared__ Shared S;
+  const int b = blockIdx.x;
+  int n_win, k;
+  window_and_pads(a, b, kSelThreads, &n_win, &k);
+  if (k == 0) return;
+  index_part(a.scores + (int64_t)b * a.score_stride, a.n_idx, k,
+             a.sel + (int64_t)b * a.topk + n_win, S);
+}
+
+// --- split builder: several workgroups per token ----------------------------
+//
+// select_filter_kernel, workgroup (part p, token b): candidates
+// [p * kSelectPartRows, (p + 1) * kSelectPartRows), 16 contiguous ones per
+// thread, and the token's sample (the runs of the one-workgroup prefilter). A
+// 12-bit histogram of the sample keys gives the bound L0: the lower edge of
+// the key bucket holding the sample key of rank r0 from the top (r0 as in the
+// one-workgroup prefilter). The part's keys >= L0 are written in row order as
+// (key, row) items (the first kSelectPartCap of them) with their count.
+//
+// select_merge_kernel, one workgroup per token: the parts' items concatenated
+// in part order (so in row order); three radix passes (12, 12 and 8 bits from
+// the top) give the k-th largest key T and how many keys equal to T belong to
+// the selection; those are the first ones in row order; a block scan writes
+// the chosen rows in ascending order. When a part kept more items than its
+// capacity, fewer than k keys were kept in all (the k-th largest key lies
+// below L0), or more than kPreCap, the token runs the one-workgroup index part
+// instead. The result is exact either way.
+
+constexpr int kFiltThreads = 256;
+constexpr int kFiltRows = kSelectPartRows / kFiltThreads;  // contiguous candidates per thread
+constexpr int kDigitBins = 4096;                           // 12-bit digits
+constexpr int kLowBits = 11;                               // second digit: key bits below the first
+constexpr int kHeadWords = 64;                             // a token's head: part counts, bound
+constexpr int kBoundWord = 32;                             // head word holding the bound L0
+constexpr int kMaxParts = kSelectMaxCandidates / kSelectPartRows;
+constexpr uint32_t kNotFiltered = 0xffffffffu;             // count of a part that kept nothing
+
+static_assert(kMaxParts <= kBoundWord && kMaxParts <= 64, "part counts: one word each, one wave");
+static_assert(kFiltRows % 4 == 0, "a filter thread reads whole 16-byte vectors");
+static_assert(kPreCap < (1 << 16), "the merge packs two item counts in one word");
+static_assert(kDigitBins <= kCopies * kBins && (1 << kLowBits) <= kWords, "merge histograms in LDS");
+
+__host__ __device__ __forceinline__ size_t token_ws_bytes(int parts) {
+  return (size_t)kHeadWords * 4 + (size_t)parts * kSelectPartCap * 8;
+}
+
+// r0 of the prefilter: the sample rank (from the top) whose key bounds the
+// kept set, or -1 when the expected keep would not fit the merge.
+__device__ __forceinline__ int sample_rank(int k, int n) {
+  const int mu = (int)(((int64_t)k * kSample) / n);
+  int r0 = mu + 4 * ((int)sqrtf((float)mu) + 1) + 8;
+  if (r0 > kSample - 1) r0 = kSample - 1;
+  if ((int64_t)(r0 + 1) * n > (int64_t)kPreCap * kSample * 3 / 4) return -1;
+  return r0;
+}
+
+// Exclusive scan of one value per thread over a workgroup of NT threads; *total
+// receives the sum. wsum holds NT / 64 words of LDS.
+template <int NT>
+__device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t base = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t ws = wsum[w];
+    base += w < wave ? ws : 0u;
+    tot += ws;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(SelectLaunch a) {
+  __shared__ uint32_t hist[kDigitBins];
+  __shared__ uint32_t wsum[kFiltThreads / 64];
+  __shared__ uint32_t s_bound;
+  const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  unsigned char* tws = static_cast<unsigned char*>(a.ws) + (size_t)b * token_ws_bytes(a.parts);
+  uint32_t* head = reinterpret_cast<uint32_t*>(tws);
+  uint2* items = reinterpret_cast<uint2*>(tws + kHeadWords * 4) + (size_t)p * kSelectPartCap;
+  const int n = a.n_idx;  // >= kSelectMinSplitRows
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  // This thread's sample run (8 keys) and its 16 candidates, loaded together
+  // with the token's position. Vectors past the last candidate re-read the
+  // last one (a valid address) and are masked.
+  const int64_t start = ((int64_t)tid * (n - 8) / (kSampleRuns - 1)) & ~(int64_t)3;
+  const float4 s0 = *reinterpret_cast<const float4*>(sc + start);
+  const float4 s1 = *reinterpret_cast<const float4*>(sc + start + 4);
+  const int row0 = p * kSelectPartRows + kFiltRows * tid;
+  const int nv = (n + 3) >> 2;
+  float4 f[kFiltRows / 4];
+#pragma unroll
+  for (int u = 0; u < kFiltRows / 4; ++u) {
+    const int v = (row0 >> 2) + u;
+    f[u] = *reinterpret_cast<const float4*>(sc + 4 * (int64_t)(v < nv ? v : nv - 1));
+  }
+  for (int i = tid; i < kDigitBins; i += kFiltThreads) hist[i] = 0u;
+  int n_win, k;
+  token_counts(a, a.pos[b], &n_win, &k);
+  const int r0 = k > 0 ? sample_rank(k, n) : -1;
+  if (r0 < 0) {  // nothing to select, or the merge takes the one-workgroup path
+    if (tid == 0) head[p] = kNotFiltered;
+    return;
+  }
+  __syncthreads();
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) atomicAdd(&hist[order_key(sv[e]) >> 20], 1u);
+  __syncthreads();
+  // The bucket of the (r0 + 1)-th largest sample key: thread t owns buckets
+  // 16 t .. 16 t + 15; the keys above its range come from a scan.
+  constexpr int kPer = kDigitBins / kFiltThreads;
+  uint32_t c = 0u;  // (reads skewed by thread: neighbours on different banks)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) c += hist[kPer * tid + ((j + tid) & (kPer - 1))];
+  uint32_t tot;
+  const uint32_t excl = wg_exclusive_scan<kFiltThreads>(c, wsum, &tot);
+  const uint32_t need = (uint32_t)r0 + 1u;
+  uint32_t above = tot - excl - c;
+  if (above < need && need <= above + c) {
+    for (int j = kPer - 1; j >= 0; --j) {
+      above += hist[kPer * tid + j];
+      if (above >= need) {
+        s_bound = (uint32_t)(kPer * tid + j) << 20;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t L0 = s_bound;  // the same in every part of the token
+  // Keep the keys >= L0, in row order.
+  uint32_t key[kFiltRows];
+  uint32_t kept = 0u;
+#pragma unroll
+  for (int u = 0; u < kFiltRows / 4; ++u) {
+    const float fv[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + 4 * u + e;
+      key[4 * u + e] = order_key(fv[e]);
+      kept |= (row < n && key[4 * u + e] >= L0) ? (1u << (4 * u + e)) : 0u;
+    }
+  }
+  uint32_t total;
+  uint32_t off = wg_exclusive_scan<kFiltThreads>((uint32_t)__popc(kept), wsum, &total);
+#pragma unroll
+  for (int j = 0; j < kFiltRows; ++j) {
+    if ((kept >> j) & 1u) {
+      if (off < (uint32_t)kSelectPartCap) items[off] = make_uint2(key[j], (uint32_t)(row0 + j));
+      ++off;
+    }
+  }
+  if (tid == 0) {
+    head[p] = total;  // more than the part holds: the merge redoes the token
+    if (p == 0) head[kBoundWord] = L0;
+  }
+}
+
+// Find the digit of a histogram of nb digits (a power of two) that holds the
+// need-th largest counted key: thread t owns digits per * t .. per * t + per - 1
+// (per = nb / threads, or one digit for threads below nb); a block scan gives
+// the keys above each range. S.prefix receives the digit and S.need the rank
+// left inside it. Every thread calls it.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t need, Shared& S) {
+  const int tid = threadIdx.x;
+  const int per = nb >= kSelThreads ? nb / kSelThreads : 1;
+  const int d0 = per * tid;
+  uint32_t c = 0u;
+  if (d0 < nb)
+    for (int j = 0; j < per; ++j) c += hist[d0 + j];
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(c, S, &tot);
+  uint32_t above = tot - excl - c;
+  if (above < need && need <= above + c) {
+    for (int j = per - 1; j >= 0; --j) {
+      const uint32_t h = hist[d0 + j];
+      if (above + h >= need) {
+        S.prefix = (uint32_t)(d0 + j);
+        S.need = need - above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+}
+
+// The k largest (key, row) items of S.pre[0, total) (key in the high word,
+// items in ascending row order, every key >= L0), ties to the lower row,
+// written to dst as rows in ascending order. hist1 holds the counts of the
+// first digit min((key - L0) >> kLowBits, kDigitBins - 1); hist2 is zero.
+__device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uint32_t* hist1,
+                             uint32_t* hist2, int32_t* dst) {
+  const int tid = threadIdx.x;
+  constexpr uint32_t kLowMask = (1u << kLowBits) - 1u;
+  find_digit(hist1, kDigitBins, (uint32_t)k, S);
+  const uint32_t d1 = S.prefix;
+  uint32_t need = S.need;
+  uint32_t T;
+  if (d1 < (uint32_t)kDigitBins - 1u) {
+    // the k-th largest key lies within 2^kLowBits of L0 + (d1 << kLowBits)
+    for (int i = tid; i < total; i += kSelThreads) {
+      const uint32_t r = (uint32_t)(S.pre[i] >> 32) - L0;
+      if ((r >> kLowBits) == d1) atomicAdd(&hist2[r & kLowMask], 1u);
+    }
+    __syncthreads();
+    find_digit(hist2, 1 << kLowBits, need, S);
+    T = L0 + (d1 << kLowBits) + S.prefix;
+    need = S.need;
+  } else {
+    // far above the bound (the last digit is a catch-all): radix over the keys
+    // of that digit, 12, 12 and 8 bits from the top
+    uint32_t prefix = 0u, mask = 0u;
+    constexpr int kShift[3] = {20, 8, 0};
+    constexpr int kBits[3] = {12, 12, 8};
+#pragma unroll
+    for (int ps = 0; ps < 3; ++ps) {
+      const int shift = kShift[ps];
+      const int nb = 1 << kBits[ps];
+      for (int i = tid; i < nb; i += kSelThreads) hist2[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < total; i += kSelThreads) {
+        const uint32_t key = (uint32_t)(S.pre[i] >> 32);
+        if (((key - L0) >> kLowBits) >= d1 && (key & mask) == prefix)
+          atomicAdd(&hist2[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_digit(hist2, nb, need, S);
+      prefix |= S.prefix << shift;
+      need = S.need;
+      mask |= (uint32_t)(nb - 1) << shift;
+      __syncthreads();
+    }
+    T = prefix;
+  }
+  // The selection: every key above T and the first `need` keys equal to T in
+  // row order. Thread t owns items [m t, m t + m), so one scan over threads of
+  // (keys above T, keys equal to T), packed in one word, places every row.
+  const int m = (total + kSelThreads - 1) / kSelThreads;
+  const int i0 = m * tid < total ? m * tid : total;
+  const int i1 = i0 + m < total ? i0 + m : total;
+  uint32_t eq = 0u, gt = 0u;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = (uint32_t)(S.pre[i] >> 32);
+    eq += key == T ? 1u : 0u;
+    gt += key > T ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t pre = block_exclusive_scan(gt << 16 | eq, S, &tot);  // counts < 2^14
+  uint32_t rank = pre & 0xffffu;          // keys equal to T before this thread
+  uint32_t off = (pre >> 16) + (rank < need ? rank : need);
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t it = S.pre[i];
+    const uint32_t key = (uint32_t)(it >> 32);
+    bool take = key > T;
+    if (key == T) take = rank++ < need;
+    if (take) dst[off++] = (int32_t)(uint32_t)it;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelectLaunch a) {
+  __shared__ Shared S;
+  __shared__ uint32_t part_cnt[kBoundWord];
+  __shared__ uint32_t part_off[kBoundWord];
+  __shared__ uint32_t s_total, s_fast;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const unsigned char* tws =
+      static_cast<const unsigned char*>(a.ws) + (size_t)b * token_ws_bytes(a.parts);
+  const uint32_t* head = reinterpret_cast<const uint32_t*>(tws);
+  const uint2* items = reinterpret_cast<const uint2*>(tws + kHeadWords * 4);
+  const int P = a.parts;
+  const int slots = P * kSelectPartCap;
+  // Every item slot, the part counts and the bound are loaded before any is
+  // needed, together with the token's position.
+  constexpr int kSlots = kMaxParts * kSelectPartCap / kSelThreads;
+  uint2 it[kSlots];
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int sl = tid + kSelThreads * u;
+    it[u] = sl < slots ? items[sl] : make_uint2(0u, 0u);
+  }
+  const uint32_t c = tid < P ? head[tid] : 0u;
+  const uint32_t L0 = head[kBoundWord];
+  uint32_t* hist1 = &S.hist[0][0];
+  uint32_t* hist2 = S.bitmap;
+  for (int i = tid; i < kDigitBins; i += kSelThreads) hist1[i] = 0u;
+  for (int i = tid; i < (1 << kLowBits); i += kSelThreads) hist2[i] = 0u;
+  int n_win, k;
+  window_and_pads(a, b, kSelThreads, &n_win, &k);
+  if (k == 0) return;
+  const float* sc = a.scores + (int64_t)b * a.score_stride;
+  int32_t* dst = a.sel + (int64_t)b * a.topk + n_win;
+  if (tid < 64) {
+    const bool bad = tid < P && c > (uint32_t)kSelectPartCap;  // includes kNotFiltered
+    const uint32_t x = wave_incl_scan(c);
+    if (tid < kBoundWord) {
+      part_cnt[tid] = c;
+      part_off[tid] = x - c;
+    }
+    const bool any_bad = __any(bad);
+    if (tid == 63) {
+      s_total = x;
+      s_fast = !any_bad && x >= (uint32_t)k && x <= (uint32_t)kPreCap;
+    }
+  }
+  __syncthreads();
+  if (!s_fast) {
+    index_part(sc, a.n_idx, k, dst, S);
+    return;
+  }
+  // Items to LDS in row order, counting the first digit on the way.
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int sl = tid + kSelThreads * u;
+    if (sl < slots) {
+      const int p = sl / kSelectPartCap, i = sl % kSelectPartCap;
+      if ((uint32_t)i < part_cnt[p]) {
+        S.pre[part_off[p] + i] = ((uint64_t)it[u].x << 32) | it[u].y;
+        const uint32_t d = (it[u].x - L0) >> kLowBits;
+        atomicAdd(&hist1[d < (uint32_t)kDigitBins ? d : (uint32_t)kDigitBins - 1u], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  select_items(S, (int)s_total, k, L0, hist1, hist2, dst);
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch& L, hipStream_t stream) {
   if (L.B <= 0 || L.k_idx > kSelectMaxK || L.n_idx > kSelectMaxCandidates) return hipErrorInvalidValue;
   hipLaunchKernelGGL(build_selection_kernel, dim3((unsigned)L.B), dim3(kSelThreads), 0, stream, L);
+  return hipGetLastError();
+}
+
+}  // namespace da
+
+namespace da {
+
+int select_parts(int n_idx) {
+  if (n_idx < kSelectMinSplitRows) return 0;
+  return (n_idx + kSelectPartRows - 1) / kSelectPartRows;
+}
+
+size_t select_workspace_bytes(int B, int n_idx) {
+  const int parts = select_parts(n_idx);
+  return parts > 0 ? (size_t)B * token_ws_bytes(parts) : 0;
+}
+
+hipError_t launch_select_split(const SelectLaunch& L, hipStream_t stream) {
+  if (L.B <= 0 || L.k_idx > kSelectMaxK || L.n_idx > kSelectMaxCandidates)
+    return hipErrorInvalidValue;
+  if (L.parts != select_parts(L.n_idx) || L.parts < 1 || !L.ws) return launch_select(L, stream);
+  hipLaunchKernelGGL(select_filter_kernel, dim3((unsigned)L.parts, (unsigned)L.B), dim3(kFiltThreads),
+                     0, stream, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)L.B), dim3(kSelThreads), 0, stream, L);
   return hipGetLastError();
 }
 

@@ -301,6 +301,35 @@ decode_attn_status decode_attn_build_selection(const decode_attn_select_problem*
                                                int32_t* sel, void* stream);
 
 /*
+ * The same selection built by several workgroups per token, for many index
+ * candidates (AttnV41 page, decode_prep_role / decode_fixed_topk: the index
+ * selection of a capturable step). Each workgroup filters a 4096-candidate part
+ * of the row against a bound taken from a sample of it and keeps the keys above
+ * the bound in a caller-owned workspace; one workgroup per token then selects
+ * among the kept keys. The output is identical to decode_attn_build_selection
+ * (exact whatever the scores: a token whose kept keys cannot hold the selection
+ * is redone over all its candidates by its merge workgroup).
+ *   workspace  device scratch of at least the bytes decode_attn_select_workspace
+ *          reports for the problem (0 for fewer than 8192 candidates, which take
+ *          the one-workgroup kernel); 16-byte aligned; contents on entry do not
+ *          matter. Two kernels on `stream`, no allocation, capturable.
+ * Returns as decode_attn_build_selection, and DA_ERR_WORKSPACE for a missing or
+ * short workspace.
+ */
+decode_attn_status decode_attn_build_selection_ws(const decode_attn_select_problem* p,
+                                                  const float* scores, const int32_t* pos,
+                                                  int32_t* sel, void* workspace,
+                                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes decode_attn_build_selection_ws needs for problem p (host
+ * only; validates the problem's shape like the build call). Returns DA_OK,
+ * DA_ERR_INVALID_ARG or DA_ERR_UNSUPPORTED.
+ */
+decode_attn_status decode_attn_select_workspace(const decode_attn_select_problem* p,
+                                                size_t* bytes);
+
+/*
  * KV append / window ring write: the current token's K and V rows go into the
  * capacity cache before the attention call, at a row read on the device
  * (fuel-dispatch page "DecodeFlashSpec", field k_len: the live length counts

@@ -1,5 +1,7 @@
 """The on-device selection builder against the selection oracle (exact, integers),
-and the built selection feeding the sparse attention, eager and in a HIP graph."""
+and the built selection feeding the sparse attention, eager and in a HIP graph.
+Every case runs both builders: one workgroup per token, and several workgroups
+per token with a caller workspace (whose contents on entry are junk)."""
 
 import numpy as np
 import pytest
@@ -23,7 +25,13 @@ def da():
     return m
 
 
-def run_builder(da, scores, pos, n_idx, k_idx, window, win_base, topk):
+def junk_workspace(da, B, n_idx, k_idx, window, topk, stride):
+    import torch
+    n = da.decode_attn_select_workspace(B, n_idx, k_idx, window, topk, stride)
+    return torch.full((max(n, 16),), 0xAB, dtype=torch.uint8, device="cuda") if n else None
+
+
+def run_builder(da, scores, pos, n_idx, k_idx, window, win_base, topk, split=False):
     import torch
     # rows padded to a multiple of 4 floats (the builder reads 16-byte vectors)
     B, n = scores.shape
@@ -33,7 +41,11 @@ def run_builder(da, scores, pos, n_idx, k_idx, window, win_base, topk):
     sc = torch.from_numpy(padded).cuda()
     ps = torch.from_numpy(np.asarray(pos, np.int32)).cuda()
     sel = torch.full((scores.shape[0], topk), 12345, dtype=torch.int32, device="cuda")
-    da.decode_attn_build_selection(sc, ps, sel, n_idx, k_idx, window, win_base)
+    if split:
+        ws = junk_workspace(da, B, n_idx, k_idx, window, topk, stride)
+        da.decode_attn_build_selection_ws(sc, ps, sel, n_idx, k_idx, window, win_base, ws)
+    else:
+        da.decode_attn_build_selection(sc, ps, sel, n_idx, k_idx, window, win_base)
     torch.cuda.synchronize()
     return sel.cpu().numpy()
 
@@ -62,16 +74,17 @@ def with_nan_payloads(s):
     return bits.view(np.float32)
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("kind", ["normal", "ties", "special"])
-def test_sparse_workload_shapes(da, kind):
+def test_sparse_workload_shapes(da, kind, split):
     # 4 tokens, 65408 index candidates, 1920 chosen, a 128-slot window ring at the
     # top of 65536 rows, launch width 2048.
     B, rows, W_, topk, k = 4, 65536, 128, 2048, 1920
     n_idx = rows - W_
     s = scores_for(80, B, n_idx, kind)
     pos = [200000, 127, 0, 50]
-    H.log(f"selection builder kind={kind}")
-    got = run_builder(da, s, pos, n_idx, k, W_, n_idx, topk)
+    H.log(f"selection builder kind={kind} split={split}")
+    got = run_builder(da, s, pos, n_idx, k, W_, n_idx, topk, split)
     want = build_selection(s, pos, n_idx, k, W_, n_idx, topk)
     assert np.array_equal(got, want)
 
@@ -85,13 +98,15 @@ def test_sparse_workload_shapes(da, kind):
     (1, 0, 5, 4, 6, [9]),                # no candidates
     (5, 1, 1, 1, 1, [0, 1, 2, 3, 4]),    # width 1: only the newest window row
 ])
-def test_edge_shapes(da, B, n_idx, k_idx, window, topk, pos):
+@pytest.mark.parametrize("split", [False, True])
+def test_edge_shapes(da, B, n_idx, k_idx, window, topk, pos, split):
     s = scores_for(81 + n_idx, B, max(n_idx, 1))
-    got = run_builder(da, s, pos, n_idx, k_idx, window, 7000, topk)
+    got = run_builder(da, s, pos, n_idx, k_idx, window, 7000, topk, split)
     assert np.array_equal(got, build_selection(s, pos, n_idx, k_idx, window, 7000, topk))
 
 
-def test_built_selection_feeds_sparse_attention(da):
+@pytest.mark.parametrize("split", [False, True])
+def test_built_selection_feeds_sparse_attention(da, split):
     import torch
     case = W.SPARSE_CASES["sparse"]
     _, (q, k, v, _) = H.sparse_case_inputs("sparse")
@@ -107,7 +122,15 @@ def test_built_selection_feeds_sparse_attention(da):
     sel = torch.empty((case.B, case.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((case.B, case.Hq, 1, case.D), dtype=torch.bfloat16, device="cuda")
     ws = da.workspace_for(plan)
-    da.decode_attn_build_selection(sc, ps, sel, n_idx, 1920, case.window, n_idx)
+    sws = junk_workspace(da, case.B, n_idx, 1920, case.window, case.topk, n_idx) if split else None
+
+    def build():
+        if split:
+            da.decode_attn_build_selection_ws(sc, ps, sel, n_idx, 1920, case.window, n_idx, sws)
+        else:
+            da.decode_attn_build_selection(sc, ps, sel, n_idx, 1920, case.window, n_idx)
+
+    build()
     da.decode_attn_sparse(plan, dq, dk, dv, sel, case.topk, out, case.scale, case.rows, ws)
     torch.cuda.synchronize()
     assert np.array_equal(sel.cpu().numpy(), sel_ref)
@@ -116,7 +139,7 @@ def test_built_selection_feeds_sparse_attention(da):
     # the same two calls captured once; scores and positions change between replays
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        da.decode_attn_build_selection(sc, ps, sel, n_idx, 1920, case.window, n_idx)
+        build()
         da.decode_attn_sparse(plan, dq, dk, dv, sel, case.topk, out, case.scale, case.rows, ws)
     for it in range(3):
         s2 = scores_for(83 + it, case.B, n_idx)
@@ -132,9 +155,11 @@ def test_built_selection_feeds_sparse_attention(da):
                           f"replay {it}")
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("k_idx,case", [(3000, "sample misleads"), (1500, "sample agrees"),
-                                        (4000, "large k"), (1920, "nan and ties")])
-def test_prefiltered_and_fallback_paths(da, k_idx, case):
+                                        (4000, "large k"), (1920, "nan and ties"),
+                                        (1920, "top in one part"), (300, "part overflow")])
+def test_prefiltered_and_fallback_paths(da, k_idx, case, split):
     # The builder first keeps the keys at or above a bound taken from a sample
     # of 256 runs of 8 keys; when fewer than k keys are kept it selects over all
     # keys instead. Giving every sampled key a huge score with k above the
@@ -150,8 +175,18 @@ def test_prefiltered_and_fallback_paths(da, k_idx, case):
         s = np.round(s * 8) / 8
         s[:, 5::301] = np.nan
         s[:, 7::211] = -np.nan
+    elif case == "top in one part":
+        # every selected key in the last 4096 candidates: that part keeps more
+        # than it can hold, and the split builder redoes the token
+        s[:, -4096:] += 50.0
+    elif case == "part overflow":
+        # a sample that lands on low scores sets a low bound: parts keep too much
+        s = np.abs(s)
+        for j in range(256):
+            start = (j * (n - 8) // 255) & ~3
+            s[:, start:start + 8] = -1.0
     pos = [-1] * B
-    got = run_builder(da, s, pos, n, k_idx, W_, 0, topk)
+    got = run_builder(da, s, pos, n, k_idx, W_, 0, topk, split)
     want = build_selection(s, pos, n, k_idx, W_, 0, topk)
     assert np.array_equal(got, want), case
 
@@ -186,11 +221,12 @@ def draw_selection_case(i):
     return dict(B=B, n=n, k=k, window=window, topk=topk, kind=kind, pos=pos), s
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("i", range(N_RANDOM))
-def test_random_selections(da, i):
+def test_random_selections(da, i, split):
     c, s = draw_selection_case(i)
     win_base = c["n"]
-    H.log(f"random selection {i}: {c}")
-    got = run_builder(da, s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"])
+    H.log(f"random selection {i} split={split}: {c}")
+    got = run_builder(da, s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"], split)
     want = build_selection(s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"])
     assert np.array_equal(got, want), c

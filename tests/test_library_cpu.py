@@ -383,3 +383,24 @@ def test_write_slots_validation(da):
     # no tokens: nothing is enqueued and no pointer is read (NULLs accepted)
     empty = da.SlotProblem(**dict(good, num_tokens=0))
     assert lib.decode_attn_write_slots(ctypes.byref(empty), None, None, None, None, None, None) == 0
+
+
+def test_split_selection_workspace_and_errors(da):
+    lib = da.library()
+    P = ctypes.c_void_p
+    # fewer than 8192 candidates: the one-workgroup builder, no workspace
+    assert da.decode_attn_select_workspace(4, 5000, 100, 16, 200) == 0
+    # 65408 candidates: 16 parts of 4096, each a 256-byte head share and 512 items of 8 bytes
+    assert da.decode_attn_select_workspace(4, 65408, 1920, 128, 2048) == 4 * (256 + 16 * 512 * 8)
+    with pytest.raises(da.DecodeAttnError):
+        da.decode_attn_select_workspace(4, 200000, 1920, 128, 2048)   # beyond 131072 candidates
+    prob = da.SelectProblem(4, 65408, 65408, 1920, 128, 65408, 2048)
+    fake = P(0x100000)
+    assert lib.decode_attn_build_selection_ws(ctypes.byref(prob), fake, fake, fake, None, 0,
+                                              None) == 3           # DA_ERR_WORKSPACE
+    assert lib.decode_attn_build_selection_ws(ctypes.byref(prob), fake, fake, fake, fake, 1024,
+                                              None) == 3
+    assert "workspace" in da.decode_attn_last_error()
+    need = 4 * (256 + 16 * 512 * 8)
+    assert lib.decode_attn_build_selection_ws(ctypes.byref(prob), fake, fake, fake, P(0x100008),
+                                              need, None) == 1     # misaligned workspace
