@@ -230,3 +230,23 @@ def test_random_selections(da, i, split):
     got = run_builder(da, s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"], split)
     want = build_selection(s, c["pos"], c["n"], c["k"], c["window"], win_base, c["topk"])
     assert np.array_equal(got, want), c
+
+
+def test_split_workspace_serves_problems_of_several_shapes(da):
+    # the split builder's workspace holds nothing between calls: one buffer
+    # serves problems of any shape in turn, junk from earlier calls left behind
+    import torch
+    shapes = [(4, 65408, 1920, 128, 2048), (2, 20000, 300, 0, 300), (7, 131072, 4096, 64, 4160),
+              (4, 65408, 1920, 128, 2048)]
+    size = max(da.decode_attn_select_workspace(*sh) for sh in shapes)
+    ws = torch.full((size,), 0xAB, dtype=torch.uint8, device="cuda")
+    for i, (B, n, k, W_, topk) in enumerate(shapes):
+        s = scores_for(600 + i, B, n)
+        pos = [13 * b + i for b in range(B)]
+        sc = torch.from_numpy(s).cuda()
+        ps = torch.from_numpy(np.asarray(pos, np.int32)).cuda()
+        sel = torch.full((B, topk), 777, dtype=torch.int32, device="cuda")
+        H.log(f"split builder shape {i}: B={B} n={n} k={k}")
+        da.decode_attn_build_selection_ws(sc, ps, sel, n, k, W_, n, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), build_selection(s, pos, n, k, W_, n, topk)), i
