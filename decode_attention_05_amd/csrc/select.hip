@@ -565,8 +565,40 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* wsum
   return base + x - v;
 }
 
+// Wave 0 alone: the bin of an LDS histogram of 64 * PER bins (16-byte
+// aligned) that holds the need-th largest counted key (need at most the
+// count), and the rank left inside that bin. Two wave-wide suffix counts and no
+// workgroup barrier: lane l sums bins PER l .. PER l + PER - 1 (its 16-byte
+// reads rotated by lane, so the lanes start on different banks), a scan picks
+// the lane range holding the key, then lane j reads bin j of that range and a
+// second scan picks the bin. Every lane returns the same values.
+template <int PER>
+__device__ __forceinline__ void wave_find_bin(const uint32_t* hist, uint32_t need, uint32_t* bin,
+                                              uint32_t* left) {
+  static_assert(PER % 4 == 0 && PER <= 64 && (PER & (PER - 1)) == 0, "bins per lane");
+  constexpr int NV = PER / 4;
+  const int lane = threadIdx.x & 63;
+  const uint4* hv = reinterpret_cast<const uint4*>(hist) + NV * lane;
+  uint32_t c = 0u;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint4 v = hv[(i + lane) & (NV - 1)];
+    c += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t incl = wave_incl_scan(c);
+  const uint32_t above = __builtin_amdgcn_readlane(incl, 63) - incl;  // keys in higher lanes
+  const int L = __builtin_ctzll(__ballot(above < need && need <= above + c));
+  const uint32_t need2 = need - __builtin_amdgcn_readlane(above, L);
+  const uint32_t x = lane < PER ? hist[PER * L + lane] : 0u;
+  const uint32_t incl2 = wave_incl_scan(x);
+  const uint32_t above2 = __builtin_amdgcn_readlane(incl2, 63) - incl2;
+  const int j = __builtin_ctzll(__ballot(above2 < need2 && need2 <= above2 + x));
+  *bin = (uint32_t)(PER * L + j);
+  *left = need2 - __builtin_amdgcn_readlane(above2, j);
+}
+
 __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(SelectLaunch a) {
-  __shared__ uint32_t hist[kDigitBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kDigitBins];
   __shared__ uint32_t wsum[kFiltThreads / 64];
   __shared__ uint32_t s_bound;
   const int p = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -602,24 +634,11 @@ __global__ __launch_bounds__(kFiltThreads) void select_filter_kernel(SelectLaunc
 #pragma unroll
   for (int e = 0; e < 8; ++e) atomicAdd(&hist[order_key(sv[e]) >> 20], 1u);
   __syncthreads();
-  // The bucket of the (r0 + 1)-th largest sample key: thread t owns buckets
-  // 16 t .. 16 t + 15; the keys above its range come from a scan.
-  constexpr int kPer = kDigitBins / kFiltThreads;
-  uint32_t c = 0u;  // (reads skewed by thread: neighbours on different banks)
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) c += hist[kPer * tid + ((j + tid) & (kPer - 1))];
-  uint32_t tot;
-  const uint32_t excl = wg_exclusive_scan<kFiltThreads>(c, wsum, &tot);
-  const uint32_t need = (uint32_t)r0 + 1u;
-  uint32_t above = tot - excl - c;
-  if (above < need && need <= above + c) {
-    for (int j = kPer - 1; j >= 0; --j) {
-      above += hist[kPer * tid + j];
-      if (above >= need) {
-        s_bound = (uint32_t)(kPer * tid + j) << 20;
-        break;
-      }
-    }
+  // The bucket of the (r0 + 1)-th largest sample key (2048 sample keys).
+  if (tid < 64) {
+    uint32_t bucket, left;
+    wave_find_bin<kDigitBins / 64>(hist, (uint32_t)r0 + 1u, &bucket, &left);
+    if (tid == 0) s_bound = bucket << 20;
   }
   __syncthreads();
   const uint32_t L0 = s_bound;  // the same in every part of the token
@@ -688,7 +707,15 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
                              uint32_t* hist2, int32_t* dst) {
   const int tid = threadIdx.x;
   constexpr uint32_t kLowMask = (1u << kLowBits) - 1u;
-  find_digit(hist1, kDigitBins, (uint32_t)k, S);
+  if (tid < 64) {
+    uint32_t d, left;
+    wave_find_bin<kDigitBins / 64>(hist1, (uint32_t)k, &d, &left);
+    if (tid == 0) {
+      S.prefix = d;
+      S.need = left;
+    }
+  }
+  __syncthreads();
   const uint32_t d1 = S.prefix;
   uint32_t need = S.need;
   uint32_t T;
@@ -699,7 +726,15 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
       if ((r >> kLowBits) == d1) atomicAdd(&hist2[r & kLowMask], 1u);
     }
     __syncthreads();
-    find_digit(hist2, 1 << kLowBits, need, S);
+    if (tid < 64) {
+      uint32_t d, left;
+      wave_find_bin<(1 << kLowBits) / 64>(hist2, need, &d, &left);
+      if (tid == 0) {
+        S.prefix = d;
+        S.need = left;
+      }
+    }
+    __syncthreads();
     T = L0 + (d1 << kLowBits) + S.prefix;
     need = S.need;
   } else {
@@ -754,7 +789,7 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelectLaunch a) {
-  __shared__ Shared S;
+  __shared__ __attribute__((aligned(16))) Shared S;
   __shared__ uint32_t part_cnt[kBoundWord];
   __shared__ uint32_t part_off[kBoundWord];
   __shared__ uint32_t s_total, s_fast;
