@@ -201,7 +201,9 @@ __device__ uint32_t radix_pass(Visit&& visit, int shift, uint32_t& prefix, uint3
 }
 
 // Block-wide exclusive scan of one value per thread (wave scans, then the
-// wave totals through LDS); *total receives the block sum.
+// wave totals through LDS); *total receives the block sum. The closing barrier
+// lets a later scan reuse S.wsum; the last scan of a kernel (kLast) skips it.
+template <bool kLast = false>
 __device__ uint32_t block_exclusive_scan(uint32_t v, Shared& S, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t x = wave_incl_scan(v);
@@ -213,7 +215,7 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, Shared& S, uint32_t* total)
     base += w < wave ? ws : 0u;
     tot += ws;
   }
-  __syncthreads();
+  if (!kLast) __syncthreads();
   *total = tot;
   return base + x - v;
 }
@@ -376,7 +378,8 @@ __device__ __forceinline__ void window_and_pads(const SelectLaunch& a, int b, in
 }
 
 // The index part of one token with one workgroup: the k (>= 1) best of the n
-// scores of row `sc`, in ascending row order, into dst[0, k).
+// scores of row `sc`, in ascending row order, into dst[0, k). The calling
+// kernel ends right after it (its last scan has no closing barrier).
 __device__ __forceinline__ void index_part(const float* sc, int n, int k, int32_t* dst, Shared& S) {
   const int tid = threadIdx.x;
   const int nwords = (n + 31) >> 5;
@@ -477,7 +480,7 @@ __device__ __forceinline__ void index_part(const float* sc, int n, int k, int32_
   uint32_t cnt = 0u;
   for (int w = w0; w < w1; ++w) cnt += __popc(S.bitmap[w]);
   uint32_t tot;
-  uint32_t off = block_exclusive_scan(cnt, S, &tot);
+  uint32_t off = block_exclusive_scan<true>(cnt, S, &tot);  // index_part ends its kernel
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = S.bitmap[w];
     while (bits) {
@@ -546,7 +549,8 @@ __device__ __forceinline__ int sample_rank(int k, int n) {
 }
 
 // Exclusive scan of one value per thread over a workgroup of NT threads; *total
-// receives the sum. wsum holds NT / 64 words of LDS.
+// receives the sum. wsum holds NT / 64 words of LDS, which are not reused (no
+// closing barrier).
 template <int NT>
 __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -560,7 +564,6 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* wsum
     base += w < wave ? ws : 0u;
     tot += ws;
   }
-  __syncthreads();
   *total = tot;
   return base + x - v;
 }
@@ -776,7 +779,7 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
     gt += key > T ? 1u : 0u;
   }
   uint32_t tot;
-  const uint32_t pre = block_exclusive_scan(gt << 16 | eq, S, &tot);  // counts < 2^14
+  const uint32_t pre = block_exclusive_scan<true>(gt << 16 | eq, S, &tot);  // counts < 2^14
   uint32_t rank = pre & 0xffffu;          // keys equal to T before this thread
   uint32_t off = (pre >> 16) + (rank < need ? rank : need);
   for (int i = i0; i < i1; ++i) {
