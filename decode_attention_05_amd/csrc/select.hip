@@ -706,8 +706,11 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
 // items in ascending row order, every key >= L0), ties to the lower row,
 // written to dst as rows in ascending order. hist1 holds the counts of the
 // first digit min((key - L0) >> kLowBits, kDigitBins - 1); hist2 is zero.
-__device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uint32_t* hist1,
-                             uint32_t* hist2, int32_t* dst) {
+// mine(fn) calls fn(key) for the keys of S.pre this thread placed (the counting
+// passes read them from registers).
+template <class Mine>
+__device__ __forceinline__ void select_items(Shared& S, int total, int k, uint32_t L0, const uint32_t* hist1,
+                             uint32_t* hist2, int32_t* dst, Mine&& mine) {
   const int tid = threadIdx.x;
   constexpr uint32_t kLowMask = (1u << kLowBits) - 1u;
   if (tid < 64) {
@@ -724,10 +727,10 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
   uint32_t T;
   if (d1 < (uint32_t)kDigitBins - 1u) {
     // the k-th largest key lies within 2^kLowBits of L0 + (d1 << kLowBits)
-    for (int i = tid; i < total; i += kSelThreads) {
-      const uint32_t r = (uint32_t)(S.pre[i] >> 32) - L0;
+    mine([&](uint32_t key) {
+      const uint32_t r = key - L0;
       if ((r >> kLowBits) == d1) atomicAdd(&hist2[r & kLowMask], 1u);
-    }
+    });
     __syncthreads();
     if (tid < 64) {
       uint32_t d, left;
@@ -752,11 +755,10 @@ __device__ void select_items(Shared& S, int total, int k, uint32_t L0, const uin
       const int nb = 1 << kBits[ps];
       for (int i = tid; i < nb; i += kSelThreads) hist2[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < total; i += kSelThreads) {
-        const uint32_t key = (uint32_t)(S.pre[i] >> 32);
+      mine([&](uint32_t key) {
         if (((key - L0) >> kLowBits) >= d1 && (key & mask) == prefix)
           atomicAdd(&hist2[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
+      });
       __syncthreads();
       find_digit(hist2, nb, need, S);
       prefix |= S.prefix << shift;
@@ -800,17 +802,18 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelectLaunch 
   const unsigned char* tws =
       static_cast<const unsigned char*>(a.ws) + (size_t)b * token_ws_bytes(a.parts);
   const uint32_t* head = reinterpret_cast<const uint32_t*>(tws);
-  const uint2* items = reinterpret_cast<const uint2*>(tws + kHeadWords * 4);
+  const uint4* items = reinterpret_cast<const uint4*>(tws + kHeadWords * 4);
   const int P = a.parts;
-  const int slots = P * kSelectPartCap;
+  const int pairs = P * kSelectPartCap / 2;  // 16-byte vectors of two (key, row) items
   // Every item slot, the part counts and the bound are loaded before any is
-  // needed, together with the token's position.
-  constexpr int kSlots = kMaxParts * kSelectPartCap / kSelThreads;
-  uint2 it[kSlots];
+  // needed, together with the token's position: vector v = tid + 1024 u holds
+  // slots 2 v and 2 v + 1.
+  constexpr int kVecs = kMaxParts * kSelectPartCap / 2 / kSelThreads;
+  uint4 it[kVecs];
 #pragma unroll
-  for (int u = 0; u < kSlots; ++u) {
-    const int sl = tid + kSelThreads * u;
-    it[u] = sl < slots ? items[sl] : make_uint2(0u, 0u);
+  for (int u = 0; u < kVecs; ++u) {
+    const int v = tid + kSelThreads * u;
+    it[u] = v < pairs ? items[v] : make_uint4(0u, 0u, 0u, 0u);
   }
   const uint32_t c = tid < P ? head[tid] : 0u;
   const uint32_t L0 = head[kBoundWord];
@@ -841,21 +844,35 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(SelectLaunch 
     index_part(sc, a.n_idx, k, dst, S);
     return;
   }
-  // Items to LDS in row order, counting the first digit on the way.
+  // Items to LDS in row order, counting the first digit on the way; bit 2 u + e
+  // of `held` marks a slot that holds an item.
+  uint32_t held = 0u;
 #pragma unroll
-  for (int u = 0; u < kSlots; ++u) {
-    const int sl = tid + kSelThreads * u;
-    if (sl < slots) {
-      const int p = sl / kSelectPartCap, i = sl % kSelectPartCap;
-      if ((uint32_t)i < part_cnt[p]) {
-        S.pre[part_off[p] + i] = ((uint64_t)it[u].x << 32) | it[u].y;
-        const uint32_t d = (it[u].x - L0) >> kLowBits;
-        atomicAdd(&hist1[d < (uint32_t)kDigitBins ? d : (uint32_t)kDigitBins - 1u], 1u);
+  for (int u = 0; u < kVecs; ++u) {
+    const int v = tid + kSelThreads * u;
+    if (v < pairs) {
+      const int p = 2 * v / kSelectPartCap, i = 2 * v % kSelectPartCap;  // i even
+      const uint32_t cnt = part_cnt[p];
+      const uint32_t key[2] = {it[u].x, it[u].z}, row[2] = {it[u].y, it[u].w};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if ((uint32_t)(i + e) < cnt) {
+          held |= 1u << (2 * u + e);
+          S.pre[part_off[p] + i + e] = ((uint64_t)key[e] << 32) | row[e];
+          const uint32_t d = (key[e] - L0) >> kLowBits;
+          atomicAdd(&hist1[d < (uint32_t)kDigitBins ? d : (uint32_t)kDigitBins - 1u], 1u);
+        }
       }
     }
   }
   __syncthreads();
-  select_items(S, (int)s_total, k, L0, hist1, hist2, dst);
+  select_items(S, (int)s_total, k, L0, hist1, hist2, dst, [&](auto fn) {
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      if ((held >> (2 * u)) & 1u) fn(it[u].x);
+      if ((held >> (2 * u + 1)) & 1u) fn(it[u].z);
+    }
+  });
 }
 
 }  // namespace
