@@ -511,14 +511,19 @@ __global__ __launch_bounds__(kSelThreads) void build_selection_kernel(SelectLaun
 // one-workgroup prefilter). The part's keys >= L0 are written in row order as
 // (key, row) items (the first kSelectPartCap of them) with their count.
 //
-// select_merge_kernel, one workgroup per token: the parts' items concatenated
-// in part order (so in row order); three radix passes (12, 12 and 8 bits from
-// the top) give the k-th largest key T and how many keys equal to T belong to
-// the selection; those are the first ones in row order; a block scan writes
-// the chosen rows in ascending order. When a part kept more items than its
-// capacity, fewer than k keys were kept in all (the k-th largest key lies
-// below L0), or more than kPreCap, the token runs the one-workgroup index part
-// instead. The result is exact either way.
+// select_merge_kernel, one workgroup per token: every item slot is loaded as
+// 16-byte vectors; the items go to LDS in part order (so in row order) while a
+// first digit min((key - L0) >> 11, 4095) is counted; one wave finds the digit
+// that holds the k-th largest key; the threads count the 11 bits below it over
+// the items they hold in registers, and one wave finds the k-th largest key T
+// and how many keys equal to T belong to the selection (the first ones in row
+// order). When that digit is the open-ended last one, three radix passes (12,
+// 12 and 8 bits from the top) over the keys at or above it find T instead. A
+// block scan of (keys above T, keys equal to T) writes the chosen rows in
+// ascending order. When a part kept more items than its capacity, fewer than k
+// keys were kept in all (the k-th largest key lies below L0), or more than
+// kPreCap, the token runs the one-workgroup index part instead. The result is
+// exact either way.
 
 constexpr int kFiltThreads = 256;
 constexpr int kFiltRows = kSelectPartRows / kFiltThreads;  // contiguous candidates per thread
