@@ -71,6 +71,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Reductions over lane pairs l, l ^ 16 and l, l ^ 32 with the gfx950 permlane
+// swaps (VALU, no LDS round trip): with both operands the same register, each
+// lane ends up holding its own value in one result and its partner's in the
+// other, so a symmetric operation of the two results reduces the pair.
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ shortx4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (shortx4 __attribute__((address_space(3)))*)(p));
@@ -160,8 +181,8 @@ __device__ __forceinline__ void tile_step(const TileRegs<D>& R, bool cut, int re
   float mx = sc[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair16_max(mx);
+  mx = pair32_max(mx);
   const float m_new = fmaxf(m, mx);
   // -inf only for a row that has seen no key yet (causal rows): then every
   // weight below is exp2(-inf) = 0 and the state stays empty.
@@ -412,8 +433,8 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair16_max(mx);
+    mx = pair32_max(mx);
     const float m_new = fmaxf(m, mx);
     // -inf only for a row that has seen no key yet (causal rows): then every
     // weight below is exp2(-inf) = 0 and the state stays empty.
@@ -471,8 +492,8 @@ __device__ __forceinline__ void attend_range(const PartialLaunch& a, unsigned ch
   }
 
   // Denominator of head r16 over the four lane groups.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = pair16_sum(l);
+  l = pair32_sum(l);
 
   __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
   float* mo = reinterpret_cast<float*>(lds);
@@ -1101,8 +1122,8 @@ __device__ __forceinline__ void wave_stream(const PartialLaunch& a, unsigned cha
     tile_step<D>(T.t, T.lim < 64, T.lim, a.Sq - 1 - r16 % a.Sq, T.q, vt, O, m, l, qscale, lane);
     if (T.flags & kTileLast) {
       // The piece's record: lane (g, r16) holds values 16 dt + 4 g .. + 3 of row r16.
-      float lt = l + __shfl_xor(l, 16);
-      lt += __shfl_xor(lt, 32);
+      float lt = pair16_sum(l);
+      lt = pair32_sum(lt);
       const bool direct = (T.flags & kTileDirect) != 0;
       const int bytes = direct ? direct_bytes : partial_bytes;
       if (pb_used + bytes > kPieceBufBytes) flush();
