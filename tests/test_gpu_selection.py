@@ -158,7 +158,9 @@ def test_built_selection_feeds_sparse_attention(da, split):
 @pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("k_idx,case", [(3000, "sample misleads"), (1500, "sample agrees"),
                                         (4000, "large k"), (1920, "nan and ties"),
-                                        (1920, "top in one part"), (300, "part overflow")])
+                                        (1920, "top in one part"), (300, "part overflow"),
+                                        (1920, "far above the bound"),
+                                        (1920, "far above the bound, ties")])
 def test_prefiltered_and_fallback_paths(da, k_idx, case, split):
     # The builder first keeps the keys at or above a bound taken from a sample
     # of 256 runs of 8 keys; when fewer than k keys are kept it selects over all
@@ -179,6 +181,18 @@ def test_prefiltered_and_fallback_paths(da, k_idx, case, split):
         # every selected key in the last 4096 candidates: that part keeps more
         # than it can hold, and the split builder redoes the token
         s[:, -4096:] += 50.0
+    elif case.startswith("far above the bound"):
+        # the selected keys sit orders of magnitude above the sample's bound, so
+        # the merge's k-th largest key lies past its first digit's range (the
+        # radix finish over the open-ended last digit); with ties, several keys
+        # share the threshold value
+        rng = np.random.Generator(np.random.PCG64(91))
+        for b in range(B):
+            rows = rng.choice(n, 2000, replace=False)
+            vals = 1.0e6 + np.arange(2000, dtype=np.float32)
+            if case.endswith("ties"):
+                vals = 1.0e6 + (np.arange(2000) // 7).astype(np.float32)
+            s[b, rows] = vals
     elif case == "part overflow":
         # a sample that lands on low scores sets a low bound: parts keep too much
         s = np.abs(s)
