@@ -3,6 +3,8 @@ and the built selection feeding the sparse attention, eager and in a HIP graph.
 Every case runs both builders: one workgroup per token, and several workgroups
 per token with a caller workspace (whose contents on entry are junk)."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -205,7 +207,9 @@ def test_prefiltered_and_fallback_paths(da, k_idx, case, split):
     assert np.array_equal(got, want), case
 
 
-N_RANDOM = 16
+# DECODE_ATTN_RANDOM_CASES widens the sweep (the draws are seeded, so a larger
+# count runs the default cases and then new ones)
+N_RANDOM = int(os.environ.get("DECODE_ATTN_RANDOM_CASES", "16"))
 
 
 def draw_selection_case(i):
