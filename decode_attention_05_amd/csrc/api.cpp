@@ -429,6 +429,19 @@ decode_attn_status decode_attn_plan(const decode_attn_problem* p, decode_attn_pl
   P.prob = *p;
   P.group = p->num_q_heads / p->num_kv_heads;
   P.kind = p->topk_max > 0 ? 1 : 0;
+  if (P.kind == 0 && p->force_splits == 0 && p->force_chunk == 0) {
+    // Tuning runs only: DECODE_ATTN_SPLITS=<n> caps the dense split count as
+    // force_splits would (anything but a positive integer is ignored).
+    const char* e = std::getenv("DECODE_ATTN_SPLITS");
+    if (e && e[0]) {
+      char* end = nullptr;
+      const long v = std::strtol(e, &end, 10);
+      if (end && *end == '\0' && v >= 1 && v <= kMaxSplits) {
+        P.prob.force_splits = (int32_t)v;
+        if (log_enabled()) std::fprintf(stderr, "[decode_attn] DECODE_ATTN_SPLITS=%ld\n", v);
+      }
+    }
+  }
   if (P.kind == 0) P.prob.kv_batch = p->batch;
   int cus = p->num_cus;
   if (cus == 0) {

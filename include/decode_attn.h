@@ -86,7 +86,10 @@ typedef struct {
   int64_t window_right; /* -1 = none; any other value -> DA_ERR_UNSUPPORTED               */
   int32_t has_softcap;  /* nonzero -> DA_ERR_UNSUPPORTED                                  */
   int32_t num_cus;      /* compute units to plan for; 0 = query the current HIP device    */
-  int32_t force_splits; /* > 0: dense split count cap (tuning and tests); 0 = heuristic   */
+  int32_t force_splits; /* > 0: dense split count cap (tuning and tests); 0 = heuristic,
+                           or for tuning runs the environment variable DECODE_ATTN_SPLITS
+                           (a positive integer) when force_chunk is 0 too; the plan's
+                           prob holds the value used                                     */
   int32_t force_chunk;  /* > 0: keys (dense) or selection entries (sparse) per split      */
   int32_t page_size;    /* 0: contiguous K/V; > 0: paged dense cache, a multiple of 32    */
   int32_t max_pages_per_seq; /* paged: block-table row length; capacity must equal

@@ -404,3 +404,19 @@ def test_split_selection_workspace_and_errors(da):
     need = 4 * (256 + 16 * 512 * 8)
     assert lib.decode_attn_build_selection_ws(ctypes.byref(prob), fake, fake, fake, P(0x100008),
                                               need, None) == 1     # misaligned workspace
+
+
+def test_split_env_override_for_tuning(da, monkeypatch):
+    # DECODE_ATTN_SPLITS caps the dense split count like force_splits (tuning
+    # runs); explicit force fields and sparse plans ignore it, as does junk
+    long = dict(num_cus=256)
+    assert da.decode_attn_plan(4, 64, 8, 128, 131072, **long).num_splits_max == 8
+    monkeypatch.setenv("DECODE_ATTN_SPLITS", "3")
+    P = da.decode_attn_plan(4, 64, 8, 128, 131072, **long)
+    assert P.num_splits_max == 3 and P.prob.force_splits == 3
+    assert da.decode_attn_plan(4, 64, 8, 128, 131072, force_splits=5, **long).num_splits_max == 5
+    sparse = da.decode_attn_plan(4, 64, 1, 128, 65536, topk_max=2048, kv_batch=1, **long)
+    assert sparse.prob.force_splits == 0 and sparse.num_splits_max == 16
+    for junk in ("0", "-2", "abc", "4x"):
+        monkeypatch.setenv("DECODE_ATTN_SPLITS", junk)
+        assert da.decode_attn_plan(4, 64, 8, 128, 131072, **long).num_splits_max == 8
