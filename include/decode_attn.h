@@ -39,6 +39,9 @@
  *     (the selection entries) are caller-owned and are not validated.
  *   - decode_attn_last_error() returns a thread-local, human-readable message
  *     for the last failing call on the calling thread.
+ *   - Environment (diagnostics and tuning runs only): DECODE_ATTN_LOG=1 prints
+ *     each plan's decisions and each call's split count to stderr;
+ *     DECODE_ATTN_SPLITS=<n> caps the dense split count (see force_splits).
  */
 #ifndef DECODE_ATTN_H
 #define DECODE_ATTN_H
